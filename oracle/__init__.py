@@ -1,0 +1,156 @@
+"""Plain CPU oracle for block-sparse tiled attention and its token-to-tile layout.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  The GPU library
+shares no code with it and never falls back to it.
+
+Two functions are defined here, each following the FastVideo fastvideo-kernel
+commit list (page 3):
+
+* ``fwd`` / ``fwd_rows`` -- block-sparse softmax attention, the plain
+  definition written out in ``bsa_oracle.c`` (binary32, as the pages' kernel
+  tests use an FP32 reference; see the 128-token sm_121a forward commit for the
+  binding's arguments and the hardening commit for the zero-row, NaN-sum and
+  padding-key rules).
+* ``tile_layout`` -- the fused layout commit's scatter of token-major Q, K, V
+  and the gate into the tile buffer in B*H*S*D order, written as the gather it
+  is equivalent to: output row t of head h reads token ``tile_src_token[t]`` of
+  that head, and a row whose source is -1 is padding and holds +0.
+
+Parity pins for both live in ``tests/test_oracle_pins.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "bsa_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+ERRORS = {
+    -1: "invalid argument",
+    -2: "key-tile index outside [0, NT)",
+    -3: "q2k_num outside [0, MS]",
+    -4: "tile length outside [0, T]",
+    -5: "out of memory",
+}
+
+
+def build() -> str:
+    """Compile the C oracle with the host compiler (IEEE semantics kept)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
+           "-ffp-contract=off", "-pthread", _SRC, "-o", _LIB + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.oracle_bsa_fwd.argtypes = [p] * 6 + [i64] * 6 + [p, i32]
+    lib.oracle_bsa_fwd.restype = i32
+    lib.oracle_bsa_fwd_rows.argtypes = [p] * 6 + [i64] * 6 + [p, i64, p, i32]
+    lib.oracle_bsa_fwd_rows.restype = i32
+    lib.oracle_softmax_scale.argtypes = [i64]
+    lib.oracle_softmax_scale.restype = ctypes.c_float
+    _lib = lib
+    return lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _prep(q, k, v, q2k_idx, q2k_num, vbs, tile):
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    q2k_num = np.ascontiguousarray(q2k_num, dtype=np.int32)
+    vbs = np.ascontiguousarray(vbs, dtype=np.int32)
+    B, H, S, D = q.shape
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share the shape [B, H, NT*T, D]")
+    if S % tile:
+        raise ValueError("sequence is not a whole number of tiles")
+    NT = S // tile
+    if q2k_num.shape != (B, H, NT) or vbs.shape != (NT,):
+        raise ValueError("q2k_num must be [B, H, NT] and block sizes [NT]")
+    if q2k_idx is None:
+        q2k_idx = np.zeros((B, H, NT, 0), np.int32)
+    q2k_idx = np.ascontiguousarray(q2k_idx, dtype=np.int32)
+    if q2k_idx.shape[:3] != (B, H, NT) or q2k_idx.ndim != 4:
+        raise ValueError("q2k_idx must be [B, H, NT, MS]")
+    MS = q2k_idx.shape[3]
+    return q, k, v, q2k_idx, q2k_num, vbs, (B, H, NT, tile, D, MS)
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def fwd(q, k, v, q2k_idx, q2k_num, vbs, tile, nthreads=None):
+    """float32 [B, H, NT*T, D]: every row of the block-sparse attention output."""
+    lib = _load()
+    q, k, v, q2k_idx, q2k_num, vbs, dims = _prep(q, k, v, q2k_idx, q2k_num, vbs, tile)
+    out = np.empty(q.shape, np.float32)
+    rc = lib.oracle_bsa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(q2k_idx), _ptr(q2k_num),
+                            _ptr(vbs), *dims, _ptr(out), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError(f"oracle rejected the problem: {ERRORS.get(rc, rc)}")
+    return out
+
+
+def fwd_rows(q, k, v, q2k_idx, q2k_num, vbs, tile, rows, nthreads=None):
+    """float32 [len(rows), D] for flat rows (b*H + h)*(NT*T) + t."""
+    lib = _load()
+    q, k, v, q2k_idx, q2k_num, vbs, dims = _prep(q, k, v, q2k_idx, q2k_num, vbs, tile)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty((rows.size, q.shape[3]), np.float32)
+    rc = lib.oracle_bsa_fwd_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(q2k_idx), _ptr(q2k_num),
+                                 _ptr(vbs), *dims, _ptr(rows), rows.size, _ptr(out),
+                                 nthreads or default_threads())
+    if rc != 0:
+        raise ValueError(f"oracle rejected the problem: {ERRORS.get(rc, rc)}")
+    return out
+
+
+def softmax_scale(head_dim: int) -> float:
+    """The binary32 scale 1/sqrt(D) the oracle multiplies q.k by."""
+    return float(_load().oracle_softmax_scale(head_dim))
+
+
+def tile_layout(srcs, tile_src_token, tile):
+    """Gather token-major [B, S_tok, H, D] tensors into [B, H, NT*T, D] tiles.
+
+    ``tile_src_token`` ([NT*T] int) names the source token of every tiled row;
+    -1 marks a padding row, which is +0.  Values are moved bit for bit.
+    """
+    tile_src_token = np.asarray(tile_src_token, dtype=np.int64)
+    if tile_src_token.ndim != 1 or tile_src_token.size % tile:
+        raise ValueError("the map must hold NT*T entries")
+    outs = []
+    for x in srcs:
+        x = np.asarray(x)
+        B, S_tok, H, D = x.shape
+        if np.any(tile_src_token >= S_tok) or np.any(tile_src_token < -1):
+            raise ValueError("map entry outside [-1, S_tok)")
+        out = np.zeros((B, H, tile_src_token.size, D), dtype=x.dtype)
+        valid = tile_src_token >= 0
+        # out[b, h, t, :] = x[b, src[t], h, :] for every valid row t
+        out[:, :, valid, :] = np.transpose(x[:, tile_src_token[valid], :, :], (0, 2, 1, 3))
+        outs.append(out)
+    return outs
