@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-sparse tiled attention hot path on one MI355X.
+
+One step = the whole path over one batch of seeded synthetic input that is
+already resident in HBM: the fused token-to-tile layout of Q, K, V and the gate
+(bsa_tile_layout, one launch) followed by the block-sparse attention forward
+(bsa_fwd, one launch).  The reported value is effective TFLOP/s counting only
+the valid tokens of the selected tiles (4*D*vbs[i]*vbs[j] per listed pair).
+
+Prints one JSON line.  Default workload: the 128-token ragged shape
+(B=1, H=12, D=128, 64 tiles of 128 with lengths U{96..128} and a last tile of
+57, 16 of 64 key tiles per query tile, 38 empty lists).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0
+METRIC = "effective TFLOPS (selected tiles only) + % bf16 MFMA peak, ms/call"
+WORKLOAD_NAMES = {
+    "ragged": "tile128_ragged_25pct",
+    "dense": "dense_limit_31200",
+    "video": "video_sparse_64tile",
+    "stress": "stress_ragged_naninf",
+    "dense25": "dense_shape_25pct",
+    "tiny": "tiny",
+}
+KERNEL_SOURCES = ["bsa_fwd.hip", "bsa_layout.hip"]
+
+
+def pair_flops(w):
+    """Valid-token FLOPs of one attention pass: sum of 4*D*vbs[i]*vbs[j] over listed pairs."""
+    live = np.arange(w.MS)[None, None, None, :] < w.q2k_num[..., None]
+    kv = np.where(live, w.vbs[w.q2k_idx], 0).sum(-1)  # [B, H, NT] valid keys per item
+    return int(4 * w.D * (kv * w.vbs[None, None, :]).sum()), kv
+
+
+def full_tile_flops(w):
+    live = np.arange(w.MS)[None, None, None, :] < w.q2k_num[..., None]
+    return int(4 * w.D * w.T * w.T * live.sum())
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "block_sparse_tiled_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if still current."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_digest") != kernel_source_digest():
+        return None  # the kernel changed since the counters were taken
+    return rec.get("fwd_bytes_per_launch")
+
+
+def cpu_threads():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS")
+    if cap and cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
+def cpu_baseline(w, kv, budget_flops):
+    """Time the CPU oracle (as is) on a bounded sample of the workload's rows."""
+    import oracle
+
+    items = np.argwhere(kv > 0)  # (b, h, i) with keys
+    rng = np.random.default_rng(0)
+    rng.shuffle(items)
+    rows, flops = [], 0
+    for b, h, i in items:
+        vq = int(w.vbs[i])
+        f = 4 * w.D * int(kv[b, h, i]) * vq
+        if flops and flops + f > budget_flops:
+            break
+        base = (b * w.H + h) * w.S + i * w.T
+        rows.extend(range(base, base + vq))
+        flops += f
+    rows = np.array(rows, np.int64)
+    threads = cpu_threads()
+    t0 = time.perf_counter()
+    oracle.fwd_rows(w.q, w.k, w.v, w.q2k_idx, w.q2k_num, w.vbs, w.T, rows, nthreads=threads)
+    dt = time.perf_counter() - t0
+    n_items = len(set((r // w.T) for r in rows))
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{n_items} query tiles ({rows.size} valid rows, {flops / 1e9:.1f} GFLOP) "
+                  f"of the same workload, random order, fp32 C oracle, {dt:.1f} s",
+        "seconds": dt,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="ragged", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-gflop", type=float, default=40.0)
+    ap.add_argument("--fwd-only", action="store_true",
+                    help="time only the attention launch (no layout) -- for profiling")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by batch*head with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_sparse_tiled_amd as bsa
+    from block_sparse_tiled_amd import inputs as gen
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating workload {args.workload}", file=sys.stderr, flush=True)
+    w = gen.make(args.workload, gate=True)
+    flops, kv = pair_flops(w)
+
+    def put(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    tok = [put(w.tok[x]) for x in ("q", "k", "v", "gate")]
+    src_map = put(w.tile_src_token)
+    idx, num, vbs = put(w.q2k_idx), put(w.q2k_num), put(w.vbs)
+    tiled = [torch.empty((w.B, w.H, w.S, w.D), dtype=torch.bfloat16, device=dev) for _ in tok]
+    out = torch.empty((w.B, w.H, w.S, w.D), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if not args.fwd_only:
+            if ev is not None:
+                ev[0].record(stream)
+            bsa.tile_layout(tok, src_map, w.T, outs=tiled)
+        if ev is not None:
+            ev[1].record(stream)
+        bsa.fwd(tiled[0], tiled[1], tiled[2], idx, num, vbs, w.T, out=out)
+        if ev is not None:
+            ev[2].record(stream)
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    fwd_ms = [events[s][1].elapsed_time(events[s][2]) for s in range(args.steps)]
+    lay_ms = ([events[s][0].elapsed_time(events[s][1]) for s in range(args.steps)]
+              if not args.fwd_only else [0.0])
+    fwd_avg = float(np.mean(fwd_ms))
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (fwd_avg * 1e-3) / 1e12
+    traffic = load_traffic(args.workload)
+
+    layout_bytes = 4 * 2 * w.D * (w.B * w.H) * (int(w.vbs.sum()) + w.S)
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOAD_NAMES[args.workload],
+            "B": w.B, "H": w.H, "D": w.D, "tile": w.T, "num_tiles": w.NT, "max_sel": w.MS,
+            "valid_tokens": int(w.vbs.sum()),
+            "flops_valid_tokens": flops,
+            "flops_full_tiles": full_tile_flops(w),
+            "step": "fwd only" if args.fwd_only else
+                    "bsa_tile_layout(q,k,v,gate) + bsa_fwd, inputs resident in HBM",
+        },
+        "pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_ms": round(fwd_avg, 5),
+        "fwd_ms_min": round(float(np.min(fwd_ms)), 5),
+        "layout_ms": round(float(np.mean(lay_ms)), 5),
+        "layout_gbs": (round(layout_bytes / (float(np.mean(lay_ms)) * 1e-3) / 1e9, 1)
+                       if not args.fwd_only else None),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "bsa_fwd_kernel",
+            "achieved": round(achieved, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+        },
+        "kernel_source_digest": kernel_source_digest(),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        cb = cpu_baseline(w, kv, args.cpu_budget_gflop * 1e9)
+        cb["value"] = round(cb["value"], 6)
+        rec["cpu_baseline"] = cb
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

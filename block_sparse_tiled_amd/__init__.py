@@ -1,1 +1,15 @@
-"""Block-sparse tiled attention for AMD Instinct MI355X (gfx950)."""
+"""Block-sparse tiled attention for AMD Instinct MI355X (gfx950).
+
+The computation lives in ``libbsa.so`` (hand-written HIP kernels behind the C
+ABI in ``include/bsa.h``); this package only marshals arguments.
+"""
+from .api import (  # noqa: F401
+    BsaError,
+    fwd,
+    fwd_out_shape,
+    load,
+    status_string,
+    tile_layout,
+    within_launch_limits,
+    within_launch_limits_py,
+)

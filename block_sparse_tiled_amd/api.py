@@ -1,0 +1,206 @@
+"""Python binding of libbsa: argument marshalling only.
+
+Every step of the computation runs in the HIP kernels behind the C ABI
+(``include/bsa.h``); this module checks torch tensors, passes their device
+pointers and sizes, and turns status codes into exceptions.  There is no
+fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbsa.so")
+
+# Launch limits, mirrored from include/bsa.h (FastVideo fastvideo-kernel commit
+# list, page 3, hardening commit: batch*heads <= 65535, rows < 2^31, tiles < 2^22).
+MAX_BATCH_HEADS = 65535
+ROWS_LIMIT = 1 << 31
+TILES_LIMIT = 1 << 22
+TILES = (64, 128)
+HEAD_DIMS = (64, 128)
+
+STATUS = {
+    0: "BSA_OK",
+    1: "BSA_ERR_INVALID_ARGUMENT",
+    2: "BSA_ERR_UNSUPPORTED_SHAPE",
+    3: "BSA_ERR_LAUNCH_LIMITS",
+    4: "BSA_ERR_NO_DEVICE",
+    5: "BSA_ERR_UNSUPPORTED_DEVICE",
+    6: "BSA_ERR_HIP",
+}
+
+
+class BsaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load():
+    """Load libbsa.so from the package directory (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m block_sparse_tiled_amd.build` "
+            "(the HIP library is required; there is no other implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.bsa_within_launch_limits.argtypes = [i64, i64, i64, i64]
+    lib.bsa_within_launch_limits.restype = ctypes.c_int
+    lib.bsa_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, i64, i64, i64, i32, i32, vp]
+    lib.bsa_fwd.restype = ctypes.c_int
+    lib.bsa_tile_layout.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp, i32,
+                                    i64, i64, i64, i64, i32, vp]
+    lib.bsa_tile_layout.restype = ctypes.c_int
+    lib.bsa_status_string.argtypes = [ctypes.c_int]
+    lib.bsa_status_string.restype = ctypes.c_char_p
+    lib.bsa_abi_version.argtypes = []
+    lib.bsa_abi_version.restype = ctypes.c_int
+    lib.bsa_test_override_arch.argtypes = [ctypes.c_char_p]
+    lib.bsa_test_override_arch.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise BsaError(status, load().bsa_status_string(status).decode())
+
+
+def status_string(status: int) -> str:
+    return load().bsa_status_string(status).decode()
+
+
+def within_launch_limits(batch: int, heads: int, rows: int, tiles: int) -> bool:
+    """The library's launch-limit check (rows = batch*heads*NT*T, tiles = NT)."""
+    return bool(load().bsa_within_launch_limits(batch, heads, rows, tiles))
+
+
+def within_launch_limits_py(batch: int, heads: int, rows: int, tiles: int) -> bool:
+    """Pure-Python mirror of the same limits, usable without the library."""
+    if min(batch, heads, rows, tiles) < 0:
+        return False
+    return batch * heads <= MAX_BATCH_HEADS and rows < ROWS_LIMIT and tiles < TILES_LIMIT
+
+
+def _stream_handle(device):
+    import torch
+
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() else ctypes.c_void_p(0)
+
+
+def _require(t, name, dtype, device, ndim):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def fwd_out_shape(q_shape):
+    """Shape of bsa.fwd's output for a q of this shape (it equals q's)."""
+    return tuple(q_shape)
+
+
+def fwd(q, k, v, q2k_idx, q2k_num, block_sizes, tile, out=None):
+    """Block-sparse tiled attention forward on the current stream.
+
+    q, k, v: bf16 [B, H, NT*tile, D] cuda tensors; q2k_idx int32 [B, H, NT, MS];
+    q2k_num int32 [B, H, NT]; block_sizes int32 [NT].  Returns ``out`` (bf16,
+    same shape as q), allocated with ``torch.empty`` when not given.
+    """
+    import torch
+
+    lib = load()
+    device = q.device
+    if device.type != "cuda":
+        raise ValueError("bsa.fwd runs on a GPU: q must be a cuda tensor")
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, name, torch.bfloat16, device, 4)
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k and v must have the same shape")
+    B, H, S, D = q.shape
+    if tile not in TILES:
+        raise ValueError(f"tile must be 64 or 128, got {tile}")
+    if S % tile:
+        raise ValueError(f"sequence length {S} is not a multiple of the tile {tile}")
+    NT = S // tile
+    _require(q2k_idx, "q2k_idx", torch.int32, device, 4)
+    _require(q2k_num, "q2k_num", torch.int32, device, 3)
+    _require(block_sizes, "block_sizes", torch.int32, device, 1)
+    if tuple(q2k_idx.shape[:3]) != (B, H, NT) or tuple(q2k_num.shape) != (B, H, NT):
+        raise ValueError("q2k_idx must be [B, H, NT, MS] and q2k_num [B, H, NT]")
+    if tuple(block_sizes.shape) != (NT,):
+        raise ValueError("block_sizes must be [NT]")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _require(out, "out", torch.bfloat16, device, 4)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    with torch.cuda.device(device):
+        _check(lib.bsa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(q2k_idx), _ptr(q2k_num),
+                           _ptr(block_sizes), tile, _ptr(out), B, H, NT, D,
+                           int(q2k_idx.shape[3]), _stream_handle(device)))
+    return out
+
+
+def tile_layout(srcs, tile_src_token, tile, outs=None):
+    """Fused token-to-tile layout of 1..4 token-major bf16 tensors [B, S_tok, H, D].
+
+    ``tile_src_token`` is an int32 cuda tensor [NT*tile] naming the source
+    token of each tile row (-1 = padding).  Returns tensors [B, H, NT*tile, D].
+    """
+    import torch
+
+    lib = load()
+    srcs = list(srcs)
+    if not 1 <= len(srcs) <= 4:
+        raise ValueError("tile_layout takes 1 to 4 tensors")
+    device = srcs[0].device
+    if device.type != "cuda":
+        raise ValueError("bsa.tile_layout runs on a GPU")
+    for n, x in enumerate(srcs):
+        _require(x, f"src[{n}]", torch.bfloat16, device, 4)
+        if x.shape != srcs[0].shape:
+            raise ValueError("all layout inputs must share one shape")
+    _require(tile_src_token, "tile_src_token", torch.int32, device, 1)
+    B, S_tok, H, D = srcs[0].shape
+    rows = tile_src_token.shape[0]
+    if tile not in TILES or rows % tile:
+        raise ValueError("the map must cover a whole number of 64- or 128-row tiles")
+    NT = rows // tile
+    if outs is None:
+        outs = [torch.empty((B, H, rows, D), dtype=torch.bfloat16, device=device) for _ in srcs]
+    else:
+        outs = list(outs)
+        if len(outs) != len(srcs):
+            raise ValueError("one output per input")
+        for n, o in enumerate(outs):
+            _require(o, f"out[{n}]", torch.bfloat16, device, 4)
+            if tuple(o.shape) != (B, H, rows, D):
+                raise ValueError("outputs must be [B, H, NT*tile, D]")
+    src_arr = (ctypes.c_void_p * len(srcs))(*[_ptr(x) for x in srcs])
+    dst_arr = (ctypes.c_void_p * len(outs))(*[_ptr(o) for o in outs])
+    with torch.cuda.device(device):
+        _check(lib.bsa_tile_layout(src_arr, dst_arr, len(srcs), _ptr(tile_src_token), tile,
+                                   B, S_tok, H, NT, D, _stream_handle(device)))
+    return outs

@@ -1,0 +1,43 @@
+// Internal interface between the C-ABI entry points (bsa_api.hip) and the
+// kernel translation units.  Arguments have been validated by the caller;
+// every launcher returns the hipError_t of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsa {
+
+struct FwdProblem {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* q2k_idx;  // may be null when max_sel == 0
+  const int32_t* q2k_num;
+  const int32_t* block_sizes;
+  uint16_t* out;
+  int64_t batch_heads;
+  int32_t num_tiles;
+  int32_t max_sel;
+  int32_t tile;
+  int32_t head_dim;
+  int32_t num_cus;  // compute units of the device, for the work mapping
+};
+
+hipError_t launch_fwd(const FwdProblem& p, hipStream_t stream);
+
+struct LayoutProblem {
+  const void* src[4];
+  void* dst[4];
+  int32_t n_tensors;
+  const int32_t* tile_src_token;
+  int64_t batch;
+  int64_t tokens;
+  int64_t heads;
+  int64_t rows_per_head;  // num_tiles * tile
+  int32_t head_dim;
+};
+
+hipError_t launch_tile_layout(const LayoutProblem& p, hipStream_t stream);
+
+}  // namespace bsa

@@ -1,0 +1,82 @@
+// Fused token-to-tile layout: token-major [B, S_tok, H, D] tensors (Q, K, V
+// and the gate) gathered into the tile buffer [B, H, NT*T, D] in one pass.
+//
+// FastVideo fastvideo-kernel commit list, page 3, fused-layout commit: one
+// kernel replaces the scatter into the tile buffer and the four transposed
+// copies that followed it.  Here the map is given in gather form (the source
+// token of every tile row, -1 for padding), which describes the same
+// permutation and lets every output byte be written exactly once, so padding
+// rows need no separate clearing pass.
+//
+// Pure HBM streaming: each thread moves one 16-byte chunk of a row for every
+// tensor, reading the map entry once.  A workgroup covers whole rows, so the
+// reads of one source row (D*2 contiguous bytes) and the writes of one tile
+// row are each coalesced.
+#include <hip/hip_runtime.h>
+
+#include "bsa_launch.h"
+
+namespace {
+
+struct Ptrs {
+  const uint4* src[4];
+  uint4* dst[4];
+};
+
+// D8 = 16-byte chunks per row (8 for D = 64, 16 for D = 128).
+template <int D8>
+__global__ __launch_bounds__(256) void tile_layout_kernel(Ptrs p, int n_tensors,
+                                                          const int32_t* __restrict__ map,
+                                                          int64_t tokens, int64_t heads,
+                                                          int64_t rows_per_head) {
+  const int64_t bh = blockIdx.y;
+  const int64_t b = bh / heads;
+  const int64_t h = bh - b * heads;
+  const int64_t chunks = rows_per_head * D8;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; c < chunks;
+       c += stride) {
+    const int64_t t = c / D8;
+    const int ch = static_cast<int>(c % D8);
+    const int32_t s = map[t];
+    const int64_t out_off = bh * chunks + c;
+    if (s >= 0 && s < tokens) {
+      const int64_t in_off = ((b * tokens + s) * heads + h) * D8 + ch;
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+        if (x < n_tensors) p.dst[x][out_off] = p.src[x][in_off];
+    } else {
+      const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+        if (x < n_tensors) p.dst[x][out_off] = zero;
+    }
+  }
+}
+
+}  // namespace
+
+namespace bsa {
+
+hipError_t launch_tile_layout(const LayoutProblem& lp, hipStream_t stream) {
+  Ptrs p;
+  for (int x = 0; x < 4; ++x) {
+    p.src[x] = static_cast<const uint4*>(lp.src[x]);
+    p.dst[x] = static_cast<uint4*>(lp.dst[x]);
+  }
+  const int d8 = lp.head_dim / 8;
+  const int64_t chunks = lp.rows_per_head * d8;
+  const int64_t want = (chunks + 255) / 256;
+  dim3 grid(static_cast<unsigned>(want < 65536 ? want : 65536),
+            static_cast<unsigned>(lp.batch * lp.heads));
+  dim3 block(256);
+  int n = lp.n_tensors;
+  const int32_t* map = lp.tile_src_token;
+  int64_t tokens = lp.tokens, heads = lp.heads, rows = lp.rows_per_head;
+  void* args[] = {&p, &n, &map, &tokens, &heads, &rows};
+  const void* fn = d8 == 16 ? reinterpret_cast<const void*>(&tile_layout_kernel<16>)
+                            : reinterpret_cast<const void*>(&tile_layout_kernel<8>);
+  return hipLaunchKernel(fn, grid, block, args, 0, stream);
+}
+
+}  // namespace bsa

@@ -1,0 +1,263 @@
+"""GPU parity of bsa_fwd against the CPU oracle, through the C ABI.
+
+Small problems are compared element by element over every row; the full-size
+configurations are compared on sampled rows (the oracle computes them one by
+one) plus properties that hold at any size: padding rows and rows without keys
+are +0 bit for bit, NaN appears exactly where the construction puts it.
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+import block_sparse_tiled_amd as bsa
+from block_sparse_tiled_amd import inputs as gen
+from parity import bits_from_dev, compare, run_fwd, sample_rows, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    bsa.load()
+    return torch.device("cuda")
+
+
+def oracle_out(oracle_mod, w, **kw):
+    return oracle_mod.fwd(w.q, w.k, w.v, w.q2k_idx, w.q2k_num, w.vbs, w.T, **kw)
+
+
+def padding_rows(w):
+    """bool [B, H, S]: query rows past their tile's valid length."""
+    r = np.arange(w.S) % w.T
+    t = np.arange(w.S) // w.T
+    return np.broadcast_to(r >= w.vbs[t], (w.B, w.H, w.S))
+
+
+def empty_list_rows(w):
+    """bool [B, H, S]: rows whose list holds no valid key (in-range contents)."""
+    tot = np.zeros((w.B, w.H, w.NT), np.int64)
+    for n in range(w.MS):
+        live = w.q2k_num > n
+        tot += np.where(live, w.vbs[w.q2k_idx[..., n]], 0)
+    return np.repeat(tot == 0, w.T, axis=2)
+
+
+def test_tiny_config(oracle_mod):
+    w = gen.tiny()
+    print(f"tiny: B={w.B} H={w.H} NT={w.NT} T={w.T} D={w.D}", flush=True)
+    got = run_fwd(w)
+    compare(got, oracle_out(oracle_mod, w), label="tiny")
+
+
+def test_ragged_config_every_row(oracle_mod):
+    w = gen.ragged()
+    print("ragged: full oracle", flush=True)
+    got = run_fwd(w)
+    mx, mean = compare(got, oracle_out(oracle_mod, w), label="ragged")
+    print(f"ragged max {mx:.3e} mean {mean:.3e}")
+
+
+@pytest.mark.parametrize("name", ["video", "dense", "dense25", "stress"])
+def test_full_size_config_sampled(oracle_mod, name):
+    w = gen.make(name)
+    print(f"{name}: B={w.B} H={w.H} NT={w.NT} T={w.T} MS={w.MS}", flush=True)
+    got = run_fwd(w)
+    D = w.D
+    extra = []
+    if "neg_inf_row" in w.notes:
+        b, h, row = w.notes["neg_inf_row"]
+        extra.append((b * w.H + h) * w.S + row)
+    rng = np.random.default_rng(123)
+    rows = sample_rows(w, 384, rng, extra)
+    ref = oracle_mod.fwd_rows(w.q, w.k, w.v, w.q2k_idx, w.q2k_num, w.vbs, w.T, rows)
+    mx, mean = compare(got.reshape(-1, D)[rows], ref, label=name)
+    print(f"{name}: {rows.size} sampled rows, max {mx:.3e} mean {mean:.3e}")
+    # properties over every row
+    zero = padding_rows(w) | empty_list_rows(w)
+    assert np.all(got[zero] == 0), "padding rows and rows without keys must be +0"
+    f = gen.bf16_bits_to_f32(got)
+    assert not np.isinf(f).any()
+    nan_rows = np.isnan(f).any(-1)
+    if "neg_inf_row" in w.notes:
+        b, h, row = w.notes["neg_inf_row"]
+        assert np.isnan(f[b, h, row]).all()
+        nan_rows[b, h, row] = False
+    assert not nan_rows.any(), f"{int(nan_rows.sum())} unexpected NaN rows"
+
+
+CASES = {
+    # name: (B, H, vbs builder, kwargs)
+    "ragged_tail": (1, 2, lambda T: [T, T - 1, T // 2 + 3, T, 7], dict(density=0.6)),
+    "odd_tiles_7": (2, 3, lambda T: [T] * 6 + [T - 5], dict(density=0.5, pad="naninf")),
+    "odd_tiles_9": (1, 2, lambda T: [T] * 8 + [T // 3], dict(density=0.4, pad="nan")),
+    "zeros_ones": (1, 2, lambda T: [0, 1, T, 1, 0, T - 3, 2], dict(density=0.7, pad="inf")),
+    "duplicates": (1, 2, lambda T: [T, 5, T, T - 9], dict(density=0.9, duplicates=True)),
+    "all_selected": (1, 2, lambda T: [T] * 5 + [T // 2], dict(counts=6)),
+    "none_selected": (1, 2, lambda T: [T] * 3, dict(counts=0)),
+    "many_waves": (2, 16, lambda T: [T] * 32 + [T - 11], dict(density=0.15)),
+}
+
+
+@pytest.mark.parametrize("T,D", [(64, 64), (64, 128), (128, 64), (128, 128)])
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_random_shapes(oracle_mod, case, T, D):
+    B, H, vbs_fn, kw = CASES[case]
+    vbs = vbs_fn(T)
+    w = gen.random_problem(zlib.crc32(f"{case}-{T}-{D}".encode()) % 10000, B=B, H=H, D=D, T=T, vbs=vbs, **kw)
+    print(f"{case}: T={T} D={D} NT={w.NT} MS={w.MS}", flush=True)
+    got = run_fwd(w)
+    compare(got, oracle_out(oracle_mod, w), label=f"{case} T={T} D={D}")
+
+
+@pytest.mark.parametrize("T,D", [(64, 128), (128, 128), (128, 64)])
+def test_padding_contents_do_not_change_a_bit(T, D):
+    w = gen.random_problem(41, B=1, H=3, D=D, T=T, vbs=[T, T - 7, 3, T, 0, T // 2], density=0.6)
+    base = run_fwd(w)
+    for pattern in ("nan", "inf", "naninf", "random"):
+        q, k, v = w.q.copy(), w.k.copy(), w.v.copy()
+        for x in (q, k, v):
+            gen.fill_padding(x, w.vbs, T, pattern)
+        print(f"padding pattern {pattern}", flush=True)
+        np.testing.assert_array_equal(run_fwd(w, q=q, k=k, v=v), base)
+
+
+def test_nan_filled_output_buffer_is_overwritten():
+    import torch
+
+    w = gen.random_problem(42, B=2, H=2, D=128, T=128, vbs=[128, 60, 0, 128], density=0.5)
+    ref = run_fwd(w)
+    out = torch.full(w.q.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    got = run_fwd(w, out=out)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_repeated_runs_are_bit_identical():
+    w = gen.make("ragged")
+    a = run_fwd(w)
+    b = run_fwd(w)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_minus_inf_tile_before_a_finite_one(oracle_mod):
+    """A listed tile whose logits are all -inf, then a finite tile: the row is finite and
+    equals the run without the -inf tile (guarded online softmax)."""
+    T, D = 64, 64
+    w = gen.random_problem(43, B=1, H=1, D=D, T=T, vbs=[T, T, T], counts=0, MS=2)
+    w.q[0, 0, 0:T, 0] = gen.to_bf16_bits(np.full(T, -1.0, np.float32))
+    w.k[0, 0, T:2 * T, 0] = gen.BF16_POS_INF
+    w.q2k_num[0, 0, 0] = 2
+    w.q2k_idx[0, 0, 0] = [1, 2]
+    ref = oracle_out(oracle_mod, w)
+    assert np.isfinite(ref[0, 0, :T]).all()
+    got = run_fwd(w)
+    compare(got, ref, label="-inf tile first")
+    w.q2k_num[0, 0, 0] = 1
+    w.q2k_idx[0, 0, 0] = [2, 0]
+    np.testing.assert_array_equal(got[0, 0, :T], run_fwd(w)[0, 0, :T])
+
+
+def test_all_minus_inf_row_is_nan(oracle_mod):
+    T, D = 128, 128
+    w = gen.random_problem(44, B=1, H=1, D=D, T=T, vbs=[T, 90, T], counts=2, MS=2, pad="naninf")
+    w.q[0, 0, 5] = 0
+    w.q[0, 0, 5, 0] = gen.BF16_NEG_INF
+    valid = gen.contiguous_map(w.vbs, T) >= 0
+    w.k[0, 0, valid, 0] = gen.to_bf16_bits(np.abs(gen.bf16_bits_to_f32(w.k[0, 0, valid, 0])) + 1)
+    got = run_fwd(w)
+    f = gen.bf16_bits_to_f32(got)
+    assert np.isnan(f[0, 0, 5]).all()
+    compare(got, oracle_out(oracle_mod, w), label="-inf row")
+
+
+def test_single_valid_key_is_exact():
+    T, D = 128, 128
+    w = gen.random_problem(45, B=1, H=2, D=D, T=T, vbs=[T, 1, T - 1], counts=1, MS=1)
+    w.q2k_idx[...] = 1
+    got = run_fwd(w)
+    for h in range(2):
+        for row in list(range(T)) + list(range(2 * T, 3 * T - 1)):
+            np.testing.assert_array_equal(got[0, h, row], w.v[0, h, T])
+
+
+def test_large_logits_stay_finite(oracle_mod):
+    """Query scaled by 20: some logits exceed log(FLT_MAX) without the max shift."""
+    w = gen.random_problem(46, B=1, H=2, D=128, T=128, vbs=[128, 100, 128, 128], density=0.8)
+    w.q[...] = gen.to_bf16_bits(gen.bf16_bits_to_f32(w.q) * 20)
+    ref = oracle_out(oracle_mod, w)
+    compare(run_fwd(w), ref, label="large logits")
+
+
+@pytest.mark.parametrize("T,D", [(64, 64), (128, 128)])
+def test_index_handling_probe(oracle_mod, T, D):
+    """Q = K = 0 gives uniform weights; V rows of tile j are the one-hot e_(j mod D), so
+    the output's non-zero pattern names exactly the listed tiles (bit-exact pattern)."""
+    NT = 24
+    vbs = [T - (3 * t) % T for t in range(NT)]
+    w = gen.random_problem(47, B=1, H=2, D=D, T=T, vbs=vbs, density=0.3)
+    w.q[...] = 0
+    w.k[...] = 0
+    w.v[...] = 0
+    one = gen.to_bf16_bits(np.float32([1.0]))[0]
+    for j in range(NT):
+        w.v[:, :, j * T: j * T + vbs[j], j % D] = one
+    ref = oracle_out(oracle_mod, w)
+    got = run_fwd(w)
+    f = gen.bf16_bits_to_f32(got)
+    np.testing.assert_array_equal(f != 0, ref != 0)
+    compare(got, ref, label="index probe")
+
+
+def test_out_of_range_contents_stay_memory_safe():
+    """Invalid device-resident contents are clamped or skipped (output unspecified)."""
+    import torch
+
+    w = gen.random_problem(48, B=1, H=2, D=64, T=64, vbs=[64, 30, 64], counts=2, MS=2)
+    idx = w.q2k_idx.copy()
+    idx[0, 0, 0] = [-5, 7]
+    idx[0, 1, 1] = [3, 1 << 30]
+    num = w.q2k_num.copy()
+    num[0, 0, 2] = 99
+    num[0, 1, 0] = -4
+    vbs = w.vbs.copy()
+    vbs[1] = 500
+    vbs[2] = -3
+    run_fwd(w, idx=idx, num=num, vbs=vbs)
+    torch.cuda.synchronize()
+
+
+def test_non_gfx950_architecture_fails_closed():
+    import torch
+
+    w = gen.random_problem(49, B=1, H=1, D=64, T=64, vbs=[64, 64], counts=1, MS=1)
+    lib = bsa.load()
+    sentinel = torch.full(w.q.shape, 7.0, dtype=torch.bfloat16, device="cuda")
+    lib.bsa_test_override_arch(b"gfx942")
+    try:
+        with pytest.raises(bsa.BsaError) as e:
+            run_fwd(w, out=sentinel)
+        assert e.value.status == 5
+        with pytest.raises(bsa.BsaError):
+            bsa.tile_layout([to_dev(w.tok["q"])], to_dev(w.tile_src_token), 64)
+    finally:
+        lib.bsa_test_override_arch(None)
+    torch.cuda.synchronize()
+    assert bool((sentinel == 7.0).all()), "nothing may be written on a refused device"
+    run_fwd(w)  # the real architecture is restored
+
+
+def test_runs_on_a_non_default_stream(oracle_mod):
+    import torch
+
+    w = gen.random_problem(50, B=1, H=2, D=128, T=128, vbs=[128, 77, 128], density=0.7)
+    args = [to_dev(x) for x in (w.q, w.k, w.v, w.q2k_idx, w.q2k_num, w.vbs)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        out = bsa.fwd(*args, w.T)
+    s.synchronize()
+    compare(bits_from_dev(out), oracle_out(oracle_mod, w), label="side stream")
