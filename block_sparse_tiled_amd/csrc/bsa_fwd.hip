@@ -6,31 +6,49 @@
 //  - hardening commit: a NaN softmax sum yields a NaN row (test l != 0, not
 //    l > 0), rows without keys stay zero, V padding rows are zeroed on
 //    partial key chunks and key steps wholly past the valid keys are
-//    skipped, so NaN/Inf padding never reaches the output;
+//    skipped, so NaN/Inf padding never reaches the output; its QK/PV overlap
+//    (one tile's loads in flight while another is computed) is realised
+//    here with LDS DMA;
 //  - Attn-QAT commit: full key tiles run without bounds masks and only the
 //    partial tail tile takes the masked step.
 //
-// Work mapping: one workgroup per (batch*head, query tile); T/32 waves, each
-// owning 32 query rows.  For every listed key tile the workgroup stages K
-// (row-major) and V (transposed, keys contiguous) in LDS, then each wave
-// computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 so that every lane
-// holds the logits of ONE query (16 keys per 32-key block, the other 16 in
-// lane^32): the row max and row sum are in-lane reductions plus one exchange
-// between the two half-waves.  The online softmax runs in the exp2 domain
-// with scale*log2(e) folded into one FMA, and O^T += V^T P^T accumulates in
-// fp32 MFMA accumulators.  P is rounded to bf16 for the second product.
+// Work mapping.  One workgroup per (batch*head, query tile) with T/32 waves,
+// each wave owning 32 query rows.  Workgroups are renumbered so that each of
+// the 8 XCDs (dispatched round-robin by linear workgroup id) receives a
+// contiguous run of work items, i.e. whole heads: the key tiles a head's
+// lists share then stay in that XCD's L2.
+//
+// Data movement.  K and V tiles are copied HBM -> LDS with LDS DMA
+// (global_load_lds_dwordx4, 16 bytes per lane, no registers).  Rows are dense
+// in LDS with the 16-byte chunks of each row XOR-swizzled by the row index so
+// that the MFMA operand reads are free of bank conflicts.  One K and one V
+// buffer per workgroup: K(n+1) is requested as soon as every wave has
+// finished reading K(n) and lands during the softmax and P.V of tile n;
+// V(n+1) is requested after P.V(n) and lands during Q.K(n+1).
+//
+// Math.  Each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so
+// every lane holds the logits of ONE query (16 keys per 32-key block, the
+// other 16 in lane^32): the row max is an in-lane reduction plus one
+// v_permlane32_swap, and the running sum stays split across the two halves
+// until the end.  The online softmax runs in the exp2 domain with
+// scale*log2(e) folded into one FMA; P is rounded to bf16 once and both the
+// row sum (v_dot2 with ones) and O^T += V^T P^T use those rounded values.
+// V^T operands come straight from the row-major V tile through the LDS
+// transpose read ds_read_b64_tr_b16.
 //
 // MFMA register layouts relied on (v_mfma_f32_32x32x16_bf16, wave64):
 //   A (32 x 16): lane l holds A[l % 32][8*(l/32) + e], e = 0..7
 //   B (16 x 32): lane l holds B[8*(l/32) + e][l % 32]
 //   C (32 x 32): lane l, register r holds C[8*(r/4) + 4*(l/32) + r%4][l % 32]
-// A and B share the k-mapping, so any permutation of the contraction index
-// applied to both is harmless; the V^T tile in LDS is stored in exactly the
-// key order in which the logits sit in the accumulator registers.
+// A and B share the k-mapping, so a permutation of the contraction index
+// applied to both is harmless: element e of half h of a 16-key chunk stands
+// for key 8*(e/4) + 4*h + e%4, the order in which S^T leaves the keys.
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element e
+// from the 8 bytes addressed by lane 4*e + i/4, at position i%4.
 //
 // Special values (exact, matching the plain definition):
 //   - masked logits are SELECTED to -inf (never added), so NaN/Inf in padding
-//     K rows cannot leak; padding V rows are written as zero in LDS;
+//     K rows cannot leak; padding V rows are overwritten with zeros in LDS;
 //   - while the running max is -inf the exponent offset is 0, so -inf logits
 //     give p = 0 and NaN logits give NaN; a NaN or +inf logit makes l NaN;
 //   - the final row is 0 without keys, NaN when keys exist but l == 0 (all
@@ -42,7 +60,12 @@
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -50,51 +73,143 @@ template <int T, int D>
 struct Cfg {
   static constexpr int kWaves = T / 32;
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kKStride = D + 8;  // bf16 per K row in LDS (+16 B: no bank conflicts)
-  static constexpr int kVStride = T + 8;  // bf16 per V^T row in LDS
-  static constexpr int kKBytes = T * kKStride * 2;
-  static constexpr int kLdsBytes = kKBytes + D * kVStride * 2;
-  static constexpr int kKeyBlocks = T / 32;  // 32-key blocks of S^T
-  static constexpr int kKSteps = D / 16;     // k-steps of the QK^T product
-  static constexpr int kDBlocks = D / 32;    // 32-row blocks of O^T
-  static constexpr int kChunks = D / 8;      // 16-byte chunks per row
+  static constexpr int kChunks = D / 8;                            // 16-byte chunks per row
+  static constexpr int kDmaPerTile = T * D * 2 / (kThreads * 16);  // per thread, per tensor
+  static constexpr int kKeyBlocks = T / 32;                        // 32-key blocks of S^T
+  static constexpr int kKSteps = D / 16;                           // k-steps of Q.K^T
+  static constexpr int kDBlocks = D / 32;                          // 32-row blocks of O^T
+  static constexpr int kKeyChunks = T / 16;                        // 16-key steps of P.V
 };
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) {
   return x < lo ? lo : (x > hi ? hi : x);
 }
 
-// Position of key `key` (a multiple of 4) inside the V^T row: within every
-// group of 16 keys the quads are stored in the order 0, 2, 1, 3, so that the
-// 8 consecutive positions a half-wave reads hold keys {4h..4h+3, 8+4h..8+4h+3},
-// the keys its accumulator registers 8g'..8g'+7 hold.
-__device__ __forceinline__ int vt_pos(int key) {
-  const int qd = (key >> 2) & 3;
-  return (key & ~15) + 4 * (((qd & 1) << 1) | (qd >> 1));
+// Chunk swizzles (16-byte chunks within a row).  K: the 8 lanes of a
+// ds_read_b128 phase read 8 consecutive rows at one chunk.  V: a 16-lane
+// ds_read_b64_tr_b16 group reads 4 consecutive rows x 2 adjacent chunks.
+__device__ __forceinline__ int swz_k(int row) { return row & 7; }
+__device__ __forceinline__ int swz_v(int row) { return 2 * (row & 3); }
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-__device__ __forceinline__ unsigned bf16_bits(float x) {
-  __bf16 b = static_cast<__bf16>(x);  // round to nearest even
-  return static_cast<unsigned>(__builtin_bit_cast(unsigned short, b));
+// Workgroup barrier ordering LDS only (global loads in flight stay in flight).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Element offset, inside a T x D tile, of the global chunk that lane `lane`
+// copies for 1 KiB LDS block `blk`: lane p of the block fills LDS slot p, so
+// it fetches the chunk that the swizzle stores there.
+template <int D, bool kIsV>
+__device__ __forceinline__ uint32_t dma_offset(int blk, int lane) {
+  constexpr int kChunks = D / 8;
+  const int row = blk * (64 / kChunks) + lane / kChunks;
+  const int chunk = (lane % kChunks) ^ (kIsV ? swz_v(row) : swz_k(row));
+  return static_cast<uint32_t>(row * D + chunk * 8);
+}
+
+// Copy one T x D bf16 tile (rows at stride D from `src`) into `lds`, one
+// 1 KiB block per wave instruction.
+template <int T, int D, bool kIsV>
+__device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, uint16_t* lds,
+                                         int wave, int lane) {
+  using C = Cfg<T, D>;
+#pragma unroll
+  for (int it = 0; it < C::kDmaPerTile; ++it) {
+    const int blk = it * C::kWaves + wave;
+    __builtin_amdgcn_global_load_lds(src + dma_offset<D, kIsV>(blk, lane),
+                                     (lds_void_t*)(lds + blk * 512), 16, 0, 0);
+  }
+}
+
+// Zero the slots of padding rows (row >= vk) that this lane's own DMA wrote.
+template <int T, int D>
+__device__ __forceinline__ void zero_padding_rows(uint16_t* lds, int vk, int wave, int lane) {
+  using C = Cfg<T, D>;
+#pragma unroll
+  for (int it = 0; it < C::kDmaPerTile; ++it) {
+    const int p = (it * C::kWaves + wave) * 64 + lane;
+    if (p / C::kChunks >= vk) *reinterpret_cast<uint4*>(lds + p * 8) = make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+// Next usable list entry at or after n: in range and with at least one key.
+__device__ __forceinline__ int next_tile(const int32_t* __restrict__ list, int count,
+                                         const int32_t* __restrict__ vbs, int num_tiles, int T,
+                                         int& n, int& vk) {
+  for (; n < count; ++n) {
+    const int j = list[n];
+    if (j < 0 || j >= num_tiles) continue;
+    vk = clampi(vbs[j], 0, T);
+    if (vk > 0) return j;
+  }
+  return -1;
+}
+
+// max(m, a, b), ignoring quiet NaNs.  Written as asm because the compiler
+// wraps fmaxf on values it cannot prove canonical (such as MFMA results) in
+// extra canonicalising moves.  The compiler does not insert the wait states an
+// MFMA result needs before a VALU read when that read is inline asm, so the
+// first read of each MFMA output block (kFirst) carries them itself: 21 wait
+// states, more than the 32x32x16 MFMA requires.  The statements are volatile,
+// so they stay in program order and the later reads of a block follow it.
+template <bool kFirst>
+__device__ __forceinline__ float max3(float m, float a, float b) {
+  float r;
+  if (kFirst)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4\n\tv_max3_f32 %0, %1, %2, %3"
+                 : "=v"(r) : "v"(m), "v"(a), "v"(b));
+  else
+    asm volatile("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(m), "v"(a), "v"(b));
+  return r;
+}
+
+// Exchange a value between the two half-waves: afterwards (a, b) hold the
+// values of lanes (l & 31, (l & 31) + 32) in every lane l.  Written as asm:
+// the v_permlane32_swap builtin called with the same value in both operands
+// is folded as if its two results were equal.
+__device__ __forceinline__ void swap_halves(float x, float& a, float& b) {
+  a = x;
+  b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+
+__device__ __forceinline__ bf16x2_t to_bf16x2(float a, float b) {
+  return __builtin_convertvector((f32x2_t){a, b}, bf16x2_t);  // round to nearest even
 }
 
 template <int T, int D>
-__global__ __launch_bounds__(2 * T) void bsa_fwd_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const int32_t* __restrict__ q2k_idx,
-    const int32_t* __restrict__ q2k_num, const int32_t* __restrict__ vbs,
-    uint16_t* __restrict__ out, int num_tiles, int max_sel, float c) {
+__global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                    const uint16_t* __restrict__ v, const int32_t* __restrict__ q2k_idx,
+                    const int32_t* __restrict__ q2k_num, const int32_t* __restrict__ vbs,
+                    uint16_t* __restrict__ out, int num_tiles, int max_sel, int num_items,
+                    float c) {
   using C = Cfg<T, D>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[C::kLdsBytes / 2];
-  uint16_t* ks = lds;                      // [T][kKStride]
-  uint16_t* vt = lds + C::kKBytes / 2;     // [D][kVStride], keys permuted per vt_pos
+  __shared__ __attribute__((aligned(1024))) uint16_t ks[T * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t vs[T * D];
 
-  const int tile_i = blockIdx.x;
-  const int64_t bh = blockIdx.y;
+  // XCD-aware renumbering: linear id L runs on XCD L % 8; give XCD x the
+  // contiguous items [start(x), start(x) + count(x)).
+  const int L = blockIdx.x + blockIdx.y * gridDim.x;
+  const int xcd = L & 7, slot = L >> 3;
+  const int per = num_items >> 3, rem = num_items & 7;
+  const int item = xcd * per + (xcd < rem ? xcd : rem) + slot;
+  const int64_t bh = item / num_tiles;
+  const int tile_i = item - static_cast<int>(bh) * num_tiles;
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int col = lane & 31;  // query within the wave's 32 rows; key/d row of A operands
+  const int col = lane & 31;
   const int half = lane >> 5;
 
   const int64_t head_elems = static_cast<int64_t>(num_tiles) * T * D;
@@ -104,9 +219,9 @@ __global__ __launch_bounds__(2 * T) void bsa_fwd_kernel(
   uint16_t* oh = out + bh * head_elems;
 
   const int vq = clampi(vbs[tile_i], 0, T);
-  const int64_t item = bh * num_tiles + tile_i;
-  const int count = max_sel > 0 ? clampi(q2k_num[item], 0, max_sel) : 0;
-  const int32_t* list = q2k_idx + item * max_sel;
+  const int64_t item64 = bh * num_tiles + tile_i;
+  const int count = max_sel > 0 ? clampi(q2k_num[item64], 0, max_sel) : 0;
+  const int32_t* list = q2k_idx + item64 * max_sel;
 
   // Q^T operand (B of the first product): lane (query col, half) holds
   // Q[row][16*kk + 8*half + 0..7].
@@ -124,131 +239,145 @@ __global__ __launch_bounds__(2 * T) void bsa_fwd_kernel(
   for (int db = 0; db < C::kDBlocks; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+  const f32x16_t zero16 = {};
   float m_run = -INFINITY;  // running max of the raw logits of this lane's query
   float l_run = 0.0f;       // this half-wave's share of the softmax sum
   bool any_keys = false;
 
-  for (int n = 0; n < count; ++n) {
-    const int j = list[n];
-    if (j < 0 || j >= num_tiles) continue;
-    const int vk = clampi(vbs[j], 0, T);
-    if (vk == 0) continue;
+  int n = 0, vk = 0;
+  int j = next_tile(list, count, vbs, num_tiles, T, n, vk);
+  if (j >= 0) {
+    dma_tile<T, D, false>(kh + static_cast<int64_t>(j) * T * D, ks, wave, lane);
+    dma_tile<T, D, true>(vh + static_cast<int64_t>(j) * T * D, vs, wave, lane);
+  }
+
+  // Loop-invariant parts of the LDS operand addresses.
+  const int k_swz = swz_k(col);                       // rows 32*kb + col share it
+  const int tr_i = lane & 15, tr_g = (lane >> 4) & 1;
+  const int v_row = 4 * half + (tr_i >> 2);           // + 16*kc (+ 8 for the high half)
+  const int v_swz = swz_v(v_row);
+  const bf16x2_t ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+
+  while (j >= 0) {
     any_keys = true;
+    int n2 = n + 1, vk2 = 0;
+    const int j2 = next_tile(list, count, vbs, num_tiles, T, n2, vk2);
+    const int nkb = (vk + 31) >> 5;  // 32-key blocks holding valid keys
 
-    __syncthreads();  // the previous tile's LDS reads are done
-    // ---- stage K_j (rows < vk) row-major --------------------------------------
-    {
-      const uint16_t* src = kh + static_cast<int64_t>(j) * T * D;
-      for (int u = tid; u < T * C::kChunks; u += C::kThreads) {
-        const int row = u / C::kChunks, ch = u % C::kChunks;
-        if (row < vk)
-          *reinterpret_cast<uint4*>(ks + row * C::kKStride + 8 * ch) =
-              *reinterpret_cast<const uint4*>(src + row * D + 8 * ch);
-      }
-    }
-    // ---- stage V_j transposed, rows >= vk as zeros ----------------------------
-    {
-      const uint16_t* src = vh + static_cast<int64_t>(j) * T * D;
-      for (int u = tid; u < (T / 4) * C::kChunks; u += C::kThreads) {
-        const int quad = u / C::kChunks, ch = u % C::kChunks;
-        uint4 r4[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = 4 * quad + e;
-          r4[e] = row < vk ? *reinterpret_cast<const uint4*>(src + row * D + 8 * ch)
-                           : make_uint4(0u, 0u, 0u, 0u);
-        }
-        const int pos = vt_pos(4 * quad);
-        const unsigned* w0 = reinterpret_cast<const unsigned*>(&r4[0]);
-        const unsigned* w1 = reinterpret_cast<const unsigned*>(&r4[1]);
-        const unsigned* w2 = reinterpret_cast<const unsigned*>(&r4[2]);
-        const unsigned* w3 = reinterpret_cast<const unsigned*>(&r4[3]);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const int d = 8 * ch + 2 * w;
-          uint2 lo, hi;
-          lo.x = (w0[w] & 0xFFFFu) | (w1[w] << 16);
-          lo.y = (w2[w] & 0xFFFFu) | (w3[w] << 16);
-          hi.x = (w0[w] >> 16) | (w1[w] & 0xFFFF0000u);
-          hi.y = (w2[w] >> 16) | (w3[w] & 0xFFFF0000u);
-          *reinterpret_cast<uint2*>(vt + d * C::kVStride + pos) = lo;
-          *reinterpret_cast<uint2*>(vt + (d + 1) * C::kVStride + pos) = hi;
-        }
-      }
-    }
-    __syncthreads();
+    wait_vmcnt<C::kDmaPerTile>();  // K(j) has landed (V(j) may be in flight)
+    lds_barrier();
 
-    // ---- S^T = K_j Q^T: 32-key blocks past vk are skipped ---------------------
+    // ---- S^T = K_j Q^T over the blocks below vk ----------------------------------
     f32x16_t s[C::kKeyBlocks];
 #pragma unroll
     for (int kb = 0; kb < C::kKeyBlocks; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
-      if (32 * kb < vk) {
-        const uint16_t* arow = ks + (32 * kb + col) * C::kKStride + 8 * half;
+      if (kb < nkb) {
+        const uint16_t* base = ks + (32 * kb + col) * D;
 #pragma unroll
         for (int kk = 0; kk < C::kKSteps; ++kk) {
+          const int chunk = (2 * kk + half) ^ k_swz;
           const bf16x8_t a =
-              __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(arow + 16 * kk));
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[kk], s[kb], 0, 0, 0);
+              __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(base + 8 * chunk));
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[kk], kk ? s[kb] : zero16,
+                                                          0, 0, 0);
         }
       }
     }
-    // ---- mask (partial tiles only) and row max --------------------------------
-    if (vk < T) {
+    lds_barrier();  // every wave is done with K(j)
+    if (j2 >= 0) dma_tile<T, D, false>(kh + static_cast<int64_t>(j2) * T * D, ks, wave, lane);
+
+    // ---- mask the partial block, running max ---------------------------------------
+    if (vk & 31) {
+      const int kbp = vk >> 5;
+      const int lim = (vk & 31) - 4 * half;  // register r holds key 8*(r/4) + r%4 (+4*half)
 #pragma unroll
       for (int kb = 0; kb < C::kKeyBlocks; ++kb)
+        if (kb == kbp) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (key >= vk) s[kb][r] = -INFINITY;
+          for (int r = 0; r < 16; ++r)
+            if (8 * (r >> 2) + (r & 3) >= lim) s[kb][r] = -INFINITY;
         }
     }
     float mt = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < C::kKeyBlocks; ++kb)
+      if (kb < nkb) {
+        mt = max3<true>(mt, s[kb][0], s[kb][1]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+        for (int r = 2; r < 16; r += 2) mt = max3<false>(mt, s[kb][r], s[kb][r + 1]);
+      }
+    {
+      float a, b;
+      swap_halves(mt, a, b);
+      mt = fmaxf(a, b);
+    }
     const float m_new = fmaxf(m_run, mt);
     const float mc = (m_new == -INFINITY ? 0.0f : m_new) * c;
     const float alpha = __builtin_amdgcn_exp2f(m_run * c - mc);
-    float psum = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < C::kKeyBlocks; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -mc));
-        s[kb][r] = p;
-        psum += p;
-      }
-    l_run = l_run * alpha + psum;
     m_run = m_new;
+    l_run *= alpha;
+    if (__any(alpha != 1.0f)) {
 #pragma unroll
-    for (int db = 0; db < C::kDBlocks; ++db)
+      for (int db = 0; db < C::kDBlocks; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+    }
 
-    // ---- O^T += V_j^T P^T over 16-key chunks below vk -------------------------
+    // ---- V(j) in LDS: wait, blank its padding rows -----------------------------------
+    if (j2 >= 0) {
+      wait_vmcnt<C::kDmaPerTile>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    if (vk < T) zero_padding_rows<T, D>(vs, vk, wave, lane);
+    lds_barrier();
+
+    // ---- per 16-key chunk: P = exp2(S*c - m*c) in bf16, row sum, O^T += V^T P^T ------
 #pragma unroll
-    for (int kc = 0; kc < T / 16; ++kc) {
+    for (int kc = 0; kc < C::kKeyChunks; ++kc) {
       if (16 * kc < vk) {
-        bf16x8_t pb;
+        const f32x16_t& sb = s[kc >> 1];
+        const int e0 = 8 * (kc & 1);
+        bf16x2_t pp[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(s[kc >> 1][8 * (kc & 1) + e]);
+        for (int e = 0; e < 4; ++e) {
+          pp[e] = to_bf16x2(
+              __builtin_amdgcn_exp2f(__builtin_fmaf(sb[e0 + 2 * e], c, -mc)),
+              __builtin_amdgcn_exp2f(__builtin_fmaf(sb[e0 + 2 * e + 1], c, -mc)));
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(pp[e], ones, l_run, false);
+        }
+        const bf16x8_t pk = __builtin_shufflevector(
+            __builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
+            __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+        const uint16_t* vrow = vs + (16 * kc + v_row) * D;
 #pragma unroll
         for (int db = 0; db < C::kDBlocks; ++db) {
+          const int colv = 32 * db + 16 * tr_g + 4 * (tr_i & 3);
+          const int off = ((colv >> 3) ^ v_swz) * 8 + (colv & 7);
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vrow + off));
+          const i16x4_t hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vrow + 8 * D + off));
           const bf16x8_t a = __builtin_bit_cast(
-              bf16x8_t, *reinterpret_cast<const uint4*>(vt + (32 * db + col) * C::kVStride +
-                                                         16 * kc + 8 * half));
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[db], 0, 0, 0);
+              bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk, acc[db], 0, 0, 0);
         }
       }
     }
+    lds_barrier();  // every wave is done with V(j)
+    if (j2 >= 0) dma_tile<T, D, true>(vh + static_cast<int64_t>(j2) * T * D, vs, wave, lane);
+
+    j = j2;
+    vk = vk2;
+    n = n2;
   }
 
-  // ---- epilogue ----------------------------------------------------------------
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  // ---- epilogue ------------------------------------------------------------------
+  float l_tot;
+  {
+    float a, b;
+    swap_halves(l_run, a, b);
+    l_tot = a + b;
+  }
   const bool zero_row = !any_keys || qrow >= vq;
   const float inv = l_tot != 0.0f ? 1.0f / l_tot : __builtin_nanf("");
   uint16_t* dst = oh + (static_cast<int64_t>(tile_i) * T + qrow) * D + 4 * half;
@@ -256,14 +385,15 @@ __global__ __launch_bounds__(2 * T) void bsa_fwd_kernel(
   for (int db = 0; db < C::kDBlocks; ++db)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      uint2 pk;
-      const float x0 = zero_row ? 0.0f : acc[db][4 * g + 0] * inv;
-      const float x1 = zero_row ? 0.0f : acc[db][4 * g + 1] * inv;
-      const float x2 = zero_row ? 0.0f : acc[db][4 * g + 2] * inv;
-      const float x3 = zero_row ? 0.0f : acc[db][4 * g + 3] * inv;
-      pk.x = bf16_bits(x0) | (bf16_bits(x1) << 16);
-      pk.y = bf16_bits(x2) | (bf16_bits(x3) << 16);
-      *reinterpret_cast<uint2*>(dst + 32 * db + 8 * g) = pk;
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = zero_row ? 0.0f : acc[db][4 * g + e] * inv;
+      const bf16x2_t lo = to_bf16x2(x[0], x[1]);
+      const bf16x2_t hi = to_bf16x2(x[2], x[3]);
+      uint2 pkd;
+      pkd.x = __builtin_bit_cast(unsigned, lo);
+      pkd.y = __builtin_bit_cast(unsigned, hi);
+      *reinterpret_cast<uint2*>(dst + 32 * db + 8 * g) = pkd;
     }
 }
 
@@ -281,8 +411,9 @@ hipError_t launch(const bsa::FwdProblem& p, hipStream_t stream) {
   const int32_t* vbs = p.block_sizes;
   uint16_t* out = p.out;
   int nt = p.num_tiles, ms = p.max_sel;
+  int items = static_cast<int>(p.batch_heads * p.num_tiles);
   float cc = c;
-  void* args[] = {&q, &k, &v, &idx, &num, &vbs, &out, &nt, &ms, &cc};
+  void* args[] = {&q, &k, &v, &idx, &num, &vbs, &out, &nt, &ms, &items, &cc};
   return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 
