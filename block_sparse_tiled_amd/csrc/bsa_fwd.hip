@@ -85,11 +85,26 @@ __device__ __forceinline__ int clampi(int x, int lo, int hi) {
   return x < lo ? lo : (x > hi ? hi : x);
 }
 
-// Chunk swizzles (16-byte chunks within a row).  K: the 8 lanes of a
-// ds_read_b128 phase read 8 consecutive rows at one chunk.  V: a 16-lane
-// ds_read_b64_tr_b16 group reads 4 consecutive rows x 2 adjacent chunks.
-__device__ __forceinline__ int swz_k(int row) { return row & 7; }
-__device__ __forceinline__ int swz_v(int row) { return 2 * (row & 3); }
+// Chunk swizzles (16-byte chunks within a row), for an LDS of 64 banks x 4
+// bytes serving 256 bytes per clock.
+//  K: a ds_read_b128 serves 16 lanes per clock; they read 16 consecutive rows
+//     at one logical chunk, so the 16 rows must land on 16 distinct 16-byte
+//     bank groups.  D = 128: a row spans all 64 banks, XOR with row % 16.
+//     D = 64: a row spans 32 banks and row parity picks the half, so XOR the
+//     8 chunks with (row / 2) % 8.
+//  V: a ds_read_b64_tr_b16 serves 32 lanes per clock: two 16-lane groups
+//     reading 4 consecutive rows x 4 adjacent logical chunks (32 bytes each
+//     group).  XOR with 4 * (row % 4) (D = 128) gives every row its own
+//     4-chunk group; for D = 64, rows r and r + 2 share a bank half, so XOR
+//     with 4 * ((row / 2) % 2).
+template <int D>
+__device__ __forceinline__ int swz_k(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int row) {
+  return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+}
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
 template <int N>
@@ -105,40 +120,88 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Element offset, inside a T x D tile, of the global chunk that lane `lane`
+// Byte offset, inside a T x D tile, of the global chunk that lane `lane`
 // copies for 1 KiB LDS block `blk`: lane p of the block fills LDS slot p, so
 // it fetches the chunk that the swizzle stores there.
 template <int D, bool kIsV>
 __device__ __forceinline__ uint32_t dma_offset(int blk, int lane) {
   constexpr int kChunks = D / 8;
   const int row = blk * (64 / kChunks) + lane / kChunks;
-  const int chunk = (lane % kChunks) ^ (kIsV ? swz_v(row) : swz_k(row));
-  return static_cast<uint32_t>(row * D + chunk * 8);
+  const int chunk = (lane % kChunks) ^ (kIsV ? swz_v<D>(row) : swz_k<D>(row));
+  return static_cast<uint32_t>((row * D + chunk * 8) * 2);
+}
+
+// One LDS DMA instruction: 64 lanes x 16 bytes from gbase + voff into LDS at
+// lds_addr + 16 * lane.  Issued as asm so that the compiler's wait-count pass,
+// which cannot tell this workgroup's K and V buffers apart, does not add
+// full drains before unrelated LDS reads; the kernel waits explicitly.  No
+// memory clobber: the statement is volatile, so it keeps its place between
+// the barriers and fences that order it, and the index lists stay scalar
+// loads.
+__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(gbase), "s"(lds_addr)
+      : "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)p));
 }
 
 // Copy one T x D bf16 tile (rows at stride D from `src`) into `lds`, one
-// 1 KiB block per wave instruction.
+// 1 KiB block per wave instruction.  The swizzle repeats every kPeriod
+// blocks, so a lane needs at most kPeriod distinct offsets plus a uniform
+// per-block term.
 template <int T, int D, bool kIsV>
 __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, uint16_t* lds,
                                          int wave, int lane) {
   using C = Cfg<T, D>;
+  constexpr int kPeriod = kIsV ? 1 : (D == 128 ? 4 : 2);
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_address(lds));
 #pragma unroll
   for (int it = 0; it < C::kDmaPerTile; ++it) {
     const int blk = it * C::kWaves + wave;
-    __builtin_amdgcn_global_load_lds(src + dma_offset<D, kIsV>(blk, lane),
-                                     (lds_void_t*)(lds + blk * 512), 16, 0, 0);
+    const uint32_t blk_uniform = static_cast<uint32_t>(blk - blk % kPeriod);
+    dma16(src, dma_offset<D, kIsV>(blk % kPeriod, lane) + blk_uniform * 1024u, base + blk * 1024);
   }
 }
 
+// An opaque copy of x: keeps the compiler from hoisting per-iteration
+// expressions of x out of the tile loop (which costs registers it does not have).
+__device__ __forceinline__ int launder(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // Zero the slots of padding rows (row >= vk) that this lane's own DMA wrote.
+// Slot p = 64*blk + lane holds row (64*blk + lane) / kChunks: a per-lane row
+// plus a uniform one, and a per-lane address plus an immediate offset.
 template <int T, int D>
 __device__ __forceinline__ void zero_padding_rows(uint16_t* lds, int vk, int wave, int lane) {
   using C = Cfg<T, D>;
+  constexpr int kRowsPerBlock = 64 / C::kChunks;
+  const int lane_row = launder(lane) / C::kChunks;
+  uint4* slot = reinterpret_cast<uint4*>(lds) + lane;
 #pragma unroll
   for (int it = 0; it < C::kDmaPerTile; ++it) {
-    const int p = (it * C::kWaves + wave) * 64 + lane;
-    if (p / C::kChunks >= vk) *reinterpret_cast<uint4*>(lds + p * 8) = make_uint4(0u, 0u, 0u, 0u);
+    const int blk = it * C::kWaves + wave;
+    if (lane_row >= vk - blk * kRowsPerBlock) slot[blk * 64] = make_uint4(0u, 0u, 0u, 0u);
   }
+}
+
+// Uniform read of one int32 through the scalar cache.  The tile lists and
+// lengths are read-only for the whole launch; as asm the read is issued as a
+// scalar load even though the (volatile) DMA statements keep the compiler
+// from proving that, and it never touches the vector-memory counter the
+// DMA waits rely on.
+__device__ __forceinline__ int scalar_load(const int32_t* p) {
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p));
+  return v;
 }
 
 // Next usable list entry at or after n: in range and with at least one key.
@@ -146,9 +209,9 @@ __device__ __forceinline__ int next_tile(const int32_t* __restrict__ list, int c
                                          const int32_t* __restrict__ vbs, int num_tiles, int T,
                                          int& n, int& vk) {
   for (; n < count; ++n) {
-    const int j = list[n];
+    const int j = scalar_load(list + n);
     if (j < 0 || j >= num_tiles) continue;
-    vk = clampi(vbs[j], 0, T);
+    vk = clampi(scalar_load(vbs + j), 0, T);
     if (vk > 0) return j;
   }
   return -1;
@@ -187,7 +250,7 @@ __device__ __forceinline__ bf16x2_t to_bf16x2(float a, float b) {
 }
 
 template <int T, int D>
-__global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(2, T == 128 ? 2 : 4)))
 void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                     const uint16_t* __restrict__ v, const int32_t* __restrict__ q2k_idx,
                     const int32_t* __restrict__ q2k_num, const int32_t* __restrict__ vbs,
@@ -208,7 +271,7 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int col = lane & 31;
   const int half = lane >> 5;
 
@@ -233,13 +296,16 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     for (int kk = 0; kk < C::kKSteps; ++kk)
       qop[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(src + 16 * kk));
   }
+  // Q must be in registers before the first tile DMA is issued: the DMAs are
+  // invisible to the compiler's wait-count bookkeeping, and an explicit drain
+  // here keeps it from placing waits for Q inside the tile loop.
+  wait_vmcnt<0>();
 
   f32x16_t acc[C::kDBlocks];
 #pragma unroll
   for (int db = 0; db < C::kDBlocks; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
-  const f32x16_t zero16 = {};
   float m_run = -INFINITY;  // running max of the raw logits of this lane's query
   float l_run = 0.0f;       // this half-wave's share of the softmax sum
   bool any_keys = false;
@@ -252,11 +318,12 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   }
 
   // Loop-invariant parts of the LDS operand addresses.
-  const int k_swz = swz_k(col);                       // rows 32*kb + col share it
+  const int k_swz = swz_k<D>(col);  // rows 32*kb + col share it
   const int tr_i = lane & 15, tr_g = (lane >> 4) & 1;
-  const int v_row = 4 * half + (tr_i >> 2);           // + 16*kc (+ 8 for the high half)
-  const int v_swz = swz_v(v_row);
+  const int v_row = 4 * half + (tr_i >> 2);  // + 16*kc (+ 8 for the high half)
+  const int v_swz = swz_v<D>(v_row);
   const bf16x2_t ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+  const f32x16_t zero16 = {};
 
   while (j >= 0) {
     any_keys = true;
