@@ -36,7 +36,7 @@ WORKLOAD_NAMES = {
     "dense25": "dense_shape_25pct",
     "tiny": "tiny",
 }
-KERNEL_SOURCES = ["bsa_fwd.hip", "bsa_layout.hip"]
+KERNEL_SOURCES = ["bsa_fwd_common.h", "bsa_fwd.hip", "bsa_layout.hip"]
 
 
 def pair_flops(w):

@@ -1,0 +1,236 @@
+// Device helpers shared by the block-sparse attention forward kernels
+// (bsa_fwd.hip): vector types, the LDS tile layout and its
+// swizzles, LDS DMA, explicit waits and barriers, scalar list reads, and the
+// small asm pieces whose compiler-generated forms are wrong or slow.
+//
+// MFMA register layouts relied on (v_mfma_f32_32x32x16_bf16, wave64):
+//   A (32 x 16): lane l holds A[l % 32][8*(l/32) + e], e = 0..7
+//   B (16 x 32): lane l holds B[8*(l/32) + e][l % 32]
+//   C (32 x 32): lane l, register r holds C[8*(r/4) + 4*(l/32) + r%4][l % 32]
+// A and B share the k-mapping, so a permutation of the contraction index
+// applied to both is harmless: element e of half h of a 16-key chunk stands
+// for key 8*(e/4) + 4*h + e%4, the order in which S^T leaves the keys.
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element e
+// from the 8 bytes addressed by lane 4*e + i/4, at position i%4.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsa {
+namespace detail {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int T, int D>
+struct Cfg {
+  static constexpr int kWaves = T / 32;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kChunks = D / 8;                            // 16-byte chunks per row
+  static constexpr int kDmaPerTile = T * D * 2 / (kThreads * 16);  // per thread, per tensor
+  static constexpr int kKeyBlocks = T / 32;                        // 32-key blocks of S^T
+  static constexpr int kKSteps = D / 16;                           // k-steps of Q.K^T
+  static constexpr int kDBlocks = D / 32;                          // 32-row blocks of O^T
+  static constexpr int kKeyChunks = T / 16;                        // 16-key steps of P.V
+};
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) {
+  return x < lo ? lo : (x > hi ? hi : x);
+}
+
+// Chunk swizzles (16-byte chunks within a row), for an LDS of 64 banks x 4
+// bytes serving 256 bytes per clock.
+//  K: a ds_read_b128 serves 16 lanes per clock; they read 16 consecutive rows
+//     at one logical chunk, so the 16 rows must land on 16 distinct 16-byte
+//     bank groups.  D = 128: a row spans all 64 banks, XOR with row % 16.
+//     D = 64: a row spans 32 banks and row parity picks the half, so XOR the
+//     8 chunks with (row / 2) % 8.
+//  V: a ds_read_b64_tr_b16 serves 32 lanes per clock: two 16-lane groups
+//     reading 4 consecutive rows x 4 adjacent logical chunks (32 bytes each
+//     group).  XOR with 4 * (row % 4) (D = 128) gives every row its own
+//     4-chunk group; for D = 64, rows r and r + 2 share a bank half, so XOR
+//     with 4 * ((row / 2) % 2).
+template <int D>
+__device__ __forceinline__ int swz_k(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int row) {
+  return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+}
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Workgroup barrier ordering LDS only (global loads in flight stay in flight).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Byte offset, inside a T x D tile, of the global chunk that lane `lane`
+// copies for 1 KiB LDS block `blk`: lane p of the block fills LDS slot p, so
+// it fetches the chunk that the swizzle stores there.
+template <int D, bool kIsV>
+__device__ __forceinline__ uint32_t dma_offset(int blk, int lane) {
+  constexpr int kChunks = D / 8;
+  const int row = blk * (64 / kChunks) + lane / kChunks;
+  const int chunk = (lane % kChunks) ^ (kIsV ? swz_v<D>(row) : swz_k<D>(row));
+  return static_cast<uint32_t>((row * D + chunk * 8) * 2);
+}
+
+// One LDS DMA instruction: 64 lanes x 16 bytes from gbase + voff into LDS at
+// lds_addr + 16 * lane.  Issued as asm so that the compiler's wait-count pass,
+// which cannot tell this workgroup's K and V buffers apart, does not add
+// full drains before unrelated LDS reads; the kernel waits explicitly.  No
+// memory clobber: the statement is volatile, so it keeps its place between
+// the barriers and fences that order it, and the index lists stay scalar
+// loads.
+__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds_addr) {
+  // M0 carries the LDS address; the compiler's own value of M0 is restored.
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(gbase), "s"(lds_addr));
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)p));
+}
+
+// Opaque copy of a uniform value: keeps the compiler from precomputing and
+// holding every per-block address of every DMA in scalar registers.
+__device__ __forceinline__ uint32_t launder_s(uint32_t x) {
+  asm volatile("" : "+s"(x));
+  return x;
+}
+
+// Copy one T x D bf16 tile (rows at stride D from `src`) into `lds`, one
+// 1 KiB block per wave instruction.  The swizzle repeats every kPeriod
+// blocks, so a lane needs at most kPeriod distinct offsets plus a uniform
+// per-block term.
+template <int T, int D, bool kIsV>
+__device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, uint16_t* lds,
+                                         int wave, int lane) {
+  using C = Cfg<T, D>;
+  constexpr int kPeriod = kIsV ? 1 : (D == 128 ? 4 : 2);
+  const uint32_t base = launder_s(__builtin_amdgcn_readfirstlane(lds_address(lds)) + wave * 1024);
+#pragma unroll
+  for (int it = 0; it < C::kDmaPerTile; ++it) {
+    const int blk = it * C::kWaves + wave;
+    const uint32_t blk_uniform = static_cast<uint32_t>(blk - blk % kPeriod);
+    dma16(src, dma_offset<D, kIsV>(blk % kPeriod, lane) + blk_uniform * 1024u,
+          base + it * C::kWaves * 1024);
+  }
+}
+
+// An opaque copy of x: keeps the compiler from hoisting per-iteration
+// expressions of x out of the tile loop (which costs registers it does not have).
+__device__ __forceinline__ int launder(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Zero the slots of padding rows (row >= vk) that this lane's own DMA wrote.
+// Slot p = 64*blk + lane holds row (64*blk + lane) / kChunks: a per-lane row
+// plus a uniform one, and a per-lane address plus an immediate offset.
+template <int T, int D>
+__device__ __forceinline__ void zero_padding_rows(uint16_t* lds, int vk, int wave, int lane) {
+  using C = Cfg<T, D>;
+  constexpr int kRowsPerBlock = 64 / C::kChunks;
+  const int lane_row = launder(lane) / C::kChunks;
+  uint4* slot = reinterpret_cast<uint4*>(lds) + lane;
+#pragma unroll
+  for (int it = 0; it < C::kDmaPerTile; ++it) {
+    const int blk = it * C::kWaves + wave;
+    if (lane_row >= vk - blk * kRowsPerBlock) slot[blk * 64] = make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+// Uniform read of one int32 through the scalar cache.  The tile lists and
+// lengths are read-only for the whole launch; as asm the read is issued as a
+// scalar load even though the (volatile) DMA statements keep the compiler
+// from proving that, and it never touches the vector-memory counter the
+// DMA waits rely on.
+__device__ __forceinline__ int scalar_load(const int32_t* p) {
+  // the address is uniform, but the compiler may have computed it in vector
+  // registers; s_load needs it in a scalar register pair
+  // (readfirstlane returns int: widen through uint32_t, never sign-extend)
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint64_t lo =
+      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a)));
+  const uint64_t hi =
+      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32)));
+  p = reinterpret_cast<const int32_t*>((hi << 32) | lo);
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p));
+  // asm results count as divergent; say it is uniform so indices derived
+  // from it stay in scalar registers
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
+// Next usable list entry at or after n: in range and with at least one key.
+__device__ __forceinline__ int next_tile(const int32_t* __restrict__ list, int count,
+                                         const int32_t* __restrict__ vbs, int num_tiles, int T,
+                                         int& n, int& vk) {
+  for (; n < count; ++n) {
+    const int j = scalar_load(list + n);
+    if (j < 0 || j >= num_tiles) continue;
+    vk = clampi(scalar_load(vbs + j), 0, T);
+    if (vk > 0) return j;
+  }
+  return -1;
+}
+
+// max(m, a, b), ignoring quiet NaNs.  Written as asm because the compiler
+// wraps fmaxf on values it cannot prove canonical (such as MFMA results) in
+// extra canonicalising moves.  The compiler does not insert the wait states an
+// MFMA result needs before a VALU read when that read is inline asm, so the
+// first read of each MFMA output block (kFirst) carries them itself: 21 wait
+// states, more than the 32x32x16 MFMA requires.  The statements are volatile,
+// so they stay in program order and the later reads of a block follow it.
+template <bool kFirst>
+__device__ __forceinline__ float max3(float m, float a, float b) {
+  float r;
+  if (kFirst)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4\n\tv_max3_f32 %0, %1, %2, %3"
+                 : "=v"(r) : "v"(m), "v"(a), "v"(b));
+  else
+    asm volatile("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(m), "v"(a), "v"(b));
+  return r;
+}
+
+// Exchange a value between the two half-waves: afterwards (a, b) hold the
+// values of lanes (l & 31, (l & 31) + 32) in every lane l.  Written as asm:
+// the v_permlane32_swap builtin called with the same value in both operands
+// is folded as if its two results were equal.
+__device__ __forceinline__ void swap_halves(float x, float& a, float& b) {
+  a = x;
+  b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+
+__device__ __forceinline__ bf16x2_t to_bf16x2(float a, float b) {
+  return __builtin_convertvector((f32x2_t){a, b}, bf16x2_t);  // round to nearest even
+}
+
+}  // namespace detail
+}  // namespace bsa
