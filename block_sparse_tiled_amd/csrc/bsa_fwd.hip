@@ -48,6 +48,8 @@
 //     logits -inf) or l is NaN, acc / l otherwise; padding query rows are 0.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "bsa_fwd_common.h"
 #include "bsa_launch.h"
 
@@ -55,46 +57,127 @@ namespace {
 
 using namespace bsa::detail;
 
+// Copies the usable entries of list[base, base + kThreads) -- in range and
+// with at least one valid key -- into tl[] in list order, with their valid
+// lengths; returns how many there are.  One entry per thread; the order is
+// kept by a wave-level prefix count (mbcnt) plus a per-wave offset.
+template <int T, int D>
+__device__ __forceinline__ int compact_list(const int32_t* __restrict__ list, int base, int count,
+                                            const int32_t* __restrict__ vbs, int num_tiles,
+                                            int2* tl, int* wave_count, int tid, int wave,
+                                            int lane) {
+  using C = Cfg<T, D>;
+  const int e = base + tid;
+  int jj = -1, len = 0;
+  if (e < count) {
+    jj = list[e];
+    if (jj >= 0 && jj < num_tiles) len = clampi(vbs[jj], 0, T);
+  }
+  const bool ok = len > 0;
+  const uint64_t m = __ballot(ok);
+  lds_barrier();  // the previous chunk's readers of tl[] and wave_count[] are done
+  if (lane == 0) wave_count[wave] = __popcll(m);
+  lds_barrier();
+  int off = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < C::kWaves; ++w) {
+    const int cw = wave_count[w];
+    off += w < wave ? cw : 0;
+    total += cw;
+  }
+  const int pos = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                            __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
+  if (ok) tl[off + pos] = make_int2(jj, len);
+  lds_barrier();
+  (void)lane;
+  return __builtin_amdgcn_readfirstlane(total);
+}
+
+// Partials cross workgroups, and XCDs, through the workspace, which is
+// uncached device memory: plain loads, stores and device-scope atomics on it
+// go to memory and are coherent across the XCDs' separate L2 caches without
+// any cache maintenance.  (A device-scope fence would write back and
+// invalidate the whole L2 of the XCD, and with it the K and V tiles the other
+// workgroups reuse; device-coherent sc1 accesses on cached memory proved as
+// costly.)
+//
+// Partial results of a split item, one slot per segment: the unnormalised
+// accumulator in register order (float index (((wave*kDBlocks + db)*4 + r/4)
+// *64 + lane)*4 + r%4), then per lane the running max and this half-wave's
+// share of the sum, then the any-keys flag.
+template <int T, int D>
+struct Slot {
+  using C = Cfg<T, D>;
+  static constexpr int kAcc = C::kWaves * C::kDBlocks * 16 * 64;  // floats
+  static constexpr int kM = kAcc;
+  static constexpr int kL = kAcc + C::kWaves * 64;
+  static constexpr int kAny = kAcc + 2 * C::kWaves * 64;
+  static constexpr int kFloats = kAny + 64;  // keeps slots 256-byte aligned
+};
+
 template <int T, int D>
 __global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(2, T == 128 ? 2 : 4)))
 void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                     const uint16_t* __restrict__ v, const int32_t* __restrict__ q2k_idx,
                     const int32_t* __restrict__ q2k_num, const int32_t* __restrict__ vbs,
-                    uint16_t* __restrict__ out, int num_tiles, int max_sel, int num_items,
-                    float c) {
+                    uint16_t* __restrict__ out, int num_tiles, int max_sel, int n_whole,
+                    int n_whole_padded, int n_split_units, int splits, float* __restrict__ ws,
+                    int* __restrict__ counters, float c) {
   using C = Cfg<T, D>;
+  using S = Slot<T, D>;
   __shared__ __attribute__((aligned(1024))) uint16_t ks[T * D];
   __shared__ __attribute__((aligned(1024))) uint16_t vs[T * D];
+  __shared__ int2 tl[C::kThreads];  // usable list entries of the current chunk: (tile, length)
+  __shared__ int wave_count[C::kWaves];
+  __shared__ int arrival;
 
-  // XCD-aware renumbering: linear id L runs on XCD L % 8; give XCD x the
-  // contiguous items [start(x), start(x) + count(x)).
-  const int L = blockIdx.x + blockIdx.y * gridDim.x;
-  const int xcd = L & 7, slot = L >> 3;
-  const int per = num_items >> 3, rem = num_items & 7;
-  const int item = xcd * per + (xcd < rem ? xcd : rem) + slot;
-  const int64_t bh = item / num_tiles;
-  const int tile_i = item - static_cast<int>(bh) * num_tiles;
+  // Work units: items [0, n_whole) whole, one workgroup each, dispatched
+  // first; then each of the remaining items cut into `splits` list segments
+  // (segment s covers list positions [s*n/splits, (s+1)*n/splits) of the
+  // item's n = max(max_sel, 1)), whose partial results are merged.
+  // XCD-aware renumbering: linear id L runs on XCD L % 8.  Within each set,
+  // XCD x receives a contiguous run of units, i.e. whole heads, so the key
+  // tiles a head's lists share stay in that XCD's L2, and the workgroups of
+  // one XCD, started together on consecutive query tiles, sweep the same key
+  // tiles at the same time.  The first set is padded to a multiple of 8
+  // units so that the second starts on XCD 0.
+  const int L = blockIdx.x;
+  const int xcd = L & 7;
+  int item, seg = 0, nseg = 1, unit2 = 0;
+  if (L < n_whole_padded) {
+    item = xcd * (n_whole_padded >> 3) + (L >> 3);
+    if (item >= n_whole) return;  // padding unit
+  } else {
+    const int l2 = L - n_whole_padded;
+    const int per = n_split_units >> 3, rem = n_split_units & 7;
+    unit2 = xcd * per + (xcd < rem ? xcd : rem) + (l2 >> 3);
+    item = n_whole + unit2 / splits;
+    seg = unit2 - (unit2 / splits) * splits;
+    nseg = splits;
+  }
+  const int positions = max_sel > 0 ? max_sel : 1;
+  const int a = static_cast<int>(static_cast<int64_t>(seg) * positions / nseg);
+  const int b = static_cast<int>(static_cast<int64_t>(seg + 1) * positions / nseg);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int col = lane & 31;
   const int half = lane >> 5;
+  const int qrow = wave * 32 + col;
 
+  const int64_t bh = item / num_tiles;
+  const int tile_i = item - static_cast<int>(bh) * num_tiles;
   const int64_t head_elems = static_cast<int64_t>(num_tiles) * T * D;
   const uint16_t* qh = q + bh * head_elems;
   const uint16_t* kh = k + bh * head_elems;
   const uint16_t* vh = v + bh * head_elems;
-  uint16_t* oh = out + bh * head_elems;
-
-  const int vq = clampi(vbs[tile_i], 0, T);
-  const int64_t item64 = bh * num_tiles + tile_i;
-  const int count = max_sel > 0 ? clampi(q2k_num[item64], 0, max_sel) : 0;
-  const int32_t* list = q2k_idx + item64 * max_sel;
+  const int count = max_sel > 0 ? clampi(q2k_num[item], 0, max_sel) : 0;
+  const int32_t* list = q2k_idx + static_cast<int64_t>(item) * max_sel;
+  const int end = b < count ? b : count;
 
   // Q^T operand (B of the first product): lane (query col, half) holds
   // Q[row][16*kk + 8*half + 0..7].
-  const int qrow = wave * 32 + col;
   bf16x8_t qop[C::kKSteps];
   {
     const uint16_t* src = qh + (static_cast<int64_t>(tile_i) * T + qrow) * D + 8 * half;
@@ -102,26 +185,15 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     for (int kk = 0; kk < C::kKSteps; ++kk)
       qop[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(src + 16 * kk));
   }
-  // Q must be in registers before the first tile DMA is issued: the DMAs are
-  // invisible to the compiler's wait-count bookkeeping, and an explicit drain
-  // here keeps it from placing waits for Q inside the tile loop.
-  wait_vmcnt<0>();
 
   f32x16_t acc[C::kDBlocks];
 #pragma unroll
   for (int db = 0; db < C::kDBlocks; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+    for (int rr = 0; rr < 16; ++rr) acc[db][rr] = 0.0f;
   float m_run = -INFINITY;  // running max of the raw logits of this lane's query
   float l_run = 0.0f;       // this half-wave's share of the softmax sum
   bool any_keys = false;
-
-  int n = 0, vk = 0;
-  int j = next_tile(list, count, vbs, num_tiles, T, n, vk);
-  if (j >= 0) {
-    dma_tile<T, D, false>(kh + static_cast<int64_t>(j) * T * D, ks, wave, lane);
-    dma_tile<T, D, true>(vh + static_cast<int64_t>(j) * T * D, vs, wave, lane);
-  }
 
   // Loop-invariant parts of the LDS operand addresses.
   const int k_swz = swz_k<D>(col);  // rows 32*kb + col share it
@@ -130,55 +202,79 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   const int v_swz = swz_v<D>(v_row);
   const bf16x2_t ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
   const f32x16_t zero16 = {};
+  const float neg_inf = launder_f(-INFINITY);
 
-  while (j >= 0) {
-    any_keys = true;
-    int n2 = n + 1, vk2 = 0;
-    const int j2 = next_tile(list, count, vbs, num_tiles, T, n2, vk2);
-    const int nkb = (vk + 31) >> 5;  // 32-key blocks holding valid keys
-
-    wait_vmcnt<C::kDmaPerTile>();  // K(j) has landed (V(j) may be in flight)
-    lds_barrier();
-
-    // ---- S^T = K_j Q^T over the blocks below vk ----------------------------------
-    f32x16_t s[C::kKeyBlocks];
+  // K operands of k-step kk for the blocks below NKB.
+  // (the per-lane swizzle is laundered so that the addresses of all k-steps
+  // are recomputed per step rather than held in registers across the loop)
+  auto read_k = [&](auto nkb_c, int kk, bf16x8_t* dst) {
+    constexpr int NKB = decltype(nkb_c)::value;
+    const int chunk = (2 * kk + half) ^ launder(k_swz);
 #pragma unroll
-    for (int kb = 0; kb < C::kKeyBlocks; ++kb) {
-      if (kb < nkb) {
-        const uint16_t* base = ks + (32 * kb + col) * D;
+    for (int kb = 0; kb < NKB; ++kb)
+      dst[kb] = __builtin_bit_cast(
+          bf16x8_t, *reinterpret_cast<const uint4*>(ks + (32 * kb + col) * D + 8 * chunk));
+  };
+  // V^T operands of 16-key chunk kc for every 32-row block of O^T.
+  auto read_v = [&](int kc, bf16x8_t* dst) {
+    const uint16_t* vrow = vs + (16 * kc + v_row) * D;
 #pragma unroll
-        for (int kk = 0; kk < C::kKSteps; ++kk) {
-          const int chunk = (2 * kk + half) ^ k_swz;
-          const bf16x8_t a =
-              __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(base + 8 * chunk));
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[kk], kk ? s[kb] : zero16,
-                                                          0, 0, 0);
-        }
-      }
+    for (int db = 0; db < C::kDBlocks; ++db) {
+      const int colv = 32 * db + 16 * tr_g + 4 * (tr_i & 3);
+      const int off = ((colv >> 3) ^ v_swz) * 8 + (colv & 7);
+      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vrow + off));
+      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vrow + 8 * D + off));
+      dst[db] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+
+  // One tile with NKB 32-key blocks holding valid keys.  On entry K(j) is in
+  // LDS and visible, V(j) may be in flight; on exit K(j2) is in LDS and
+  // visible and V(j2) is requested.
+  auto tile_step = [&](auto nkb_c, int vk, int j2) {
+    constexpr int NKB = decltype(nkb_c)::value;
+
+    // ---- S^T = K_j Q^T, k-step outer: NKB independent accumulators, the
+    //      operands of step kk + 1 requested before the MFMAs of step kk ----------
+    f32x16_t s[NKB];
+    bf16x8_t ka[NKB], kn[NKB];
+    read_k(nkb_c, 0, ka);
+#pragma unroll
+    for (int kk = 0; kk < C::kKSteps; ++kk) {
+      if (kk + 1 < C::kKSteps) read_k(nkb_c, kk + 1, kn);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kb], qop[kk], kk ? s[kb] : zero16, 0,
+                                                        0, 0);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) ka[kb] = kn[kb];
+      __builtin_amdgcn_sched_barrier(0);  // keeps the reads one step ahead, no further
     }
     lds_barrier();  // every wave is done with K(j)
     if (j2 >= 0) dma_tile<T, D, false>(kh + static_cast<int64_t>(j2) * T * D, ks, wave, lane);
 
-    // ---- mask the partial block, running max ---------------------------------------
-    if (vk & 31) {
-      const int kbp = vk >> 5;
-      const int lim = (vk & 31) - 4 * half;  // register r holds key 8*(r/4) + r%4 (+4*half)
+    // ---- mask keys at or past vk (whole blocks included), running max ------------
+    if (vk < 32 * NKB) {
+      const int lim = vk - 4 * half;  // register r of block kb holds key 32*kb + 8*(r/4) + r%4 (+4*half)
 #pragma unroll
-      for (int kb = 0; kb < C::kKeyBlocks; ++kb)
-        if (kb == kbp) {
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (8 * (r >> 2) + (r & 3) >= lim) s[kb][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (32 * kb + 8 * (r >> 2) + (r & 3) >= lim) s[kb][r] = -INFINITY;
     }
-    float mt = -INFINITY;
+    float mx[NKB];
 #pragma unroll
-    for (int kb = 0; kb < C::kKeyBlocks; ++kb)
-      if (kb < nkb) {
-        mt = max3<true>(mt, s[kb][0], s[kb][1]);
+    for (int kb = 0; kb < NKB; ++kb)
+      mx[kb] = kb == 0 ? max3<true>(neg_inf, s[0][0], s[0][1])
+                       : max3<false>(neg_inf, s[kb][0], s[kb][1]);
 #pragma unroll
-        for (int r = 2; r < 16; r += 2) mt = max3<false>(mt, s[kb][r], s[kb][r + 1]);
-      }
+    for (int r = 2; r < 16; r += 2)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) mx[kb] = max3<false>(mx[kb], s[kb][r], s[kb][r + 1]);
+    float mt = mx[0];
+#pragma unroll
+    for (int kb = 1; kb < NKB; kb += 2)
+      mt = max3<false>(mt, mx[kb], kb + 1 < NKB ? mx[kb + 1] : mx[kb]);
     {
       float a, b;
       swap_halves(mt, a, b);
@@ -196,84 +292,189 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
     }
 
-    // ---- V(j) in LDS: wait, blank its padding rows -----------------------------------
+    // ---- V(j) in LDS: wait, blank its padding rows ---------------------------------
     if (j2 >= 0) {
-      wait_vmcnt<C::kDmaPerTile>();
+      wait_vmcnt<C::kDmaPerTile>();  // K(j2) stays in flight
     } else {
       wait_vmcnt<0>();
     }
     if (vk < T) zero_padding_rows<T, D>(vs, vk, wave, lane);
     lds_barrier();
 
-    // ---- per 16-key chunk: P = exp2(S*c - m*c) in bf16, row sum, O^T += V^T P^T ------
+    // ---- per 16-key chunk: P = exp2(S*c - m*c) in bf16, row sum, O^T += V^T P^T.
+    //      Both chunks of every block below NKB are processed: keys at or past vk
+    //      have p = 0 and zeroed V rows, so they add exact zeros.  The V operands
+    //      of chunk kc + 1 are requested before the exponentials of chunk kc. ----
+    bf16x8_t va[C::kDBlocks], vn[C::kDBlocks];
+    read_v(0, va);
 #pragma unroll
-    for (int kc = 0; kc < C::kKeyChunks; ++kc) {
-      if (16 * kc < vk) {
-        const f32x16_t& sb = s[kc >> 1];
-        const int e0 = 8 * (kc & 1);
-        bf16x2_t pp[4];
+    for (int kc = 0; kc < 2 * NKB; ++kc) {
+      if (kc + 1 < 2 * NKB) read_v(kc + 1, vn);
+      const int e0 = 8 * (kc & 1);
+      bf16x2_t pp[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pp[e] = to_bf16x2(
-              __builtin_amdgcn_exp2f(__builtin_fmaf(sb[e0 + 2 * e], c, -mc)),
-              __builtin_amdgcn_exp2f(__builtin_fmaf(sb[e0 + 2 * e + 1], c, -mc)));
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(pp[e], ones, l_run, false);
-        }
-        const bf16x8_t pk = __builtin_shufflevector(
-            __builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
-            __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
-        const uint16_t* vrow = vs + (16 * kc + v_row) * D;
-#pragma unroll
-        for (int db = 0; db < C::kDBlocks; ++db) {
-          const int colv = 32 * db + 16 * tr_g + 4 * (tr_i & 3);
-          const int off = ((colv >> 3) ^ v_swz) * 8 + (colv & 7);
-          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vrow + off));
-          const i16x4_t hi =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vrow + 8 * D + off));
-          const bf16x8_t a = __builtin_bit_cast(
-              bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk, acc[db], 0, 0, 0);
-        }
+      for (int e = 0; e < 4; ++e) {
+        pp[e] = to_bf16x2(
+            __builtin_amdgcn_exp2f(__builtin_fmaf(s[kc >> 1][e0 + 2 * e], c, -mc)),
+            __builtin_amdgcn_exp2f(__builtin_fmaf(s[kc >> 1][e0 + 2 * e + 1], c, -mc)));
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(pp[e], ones, l_run, false);
       }
+      const bf16x8_t pk = __builtin_shufflevector(
+          __builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
+          __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int db = 0; db < C::kDBlocks; ++db)
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db], pk, acc[db], 0, 0, 0);
+#pragma unroll
+      for (int db = 0; db < C::kDBlocks; ++db) va[db] = vn[db];
+      __builtin_amdgcn_sched_barrier(0);
     }
-    lds_barrier();  // every wave is done with V(j)
+
+    // ---- K(j2) landed (the only copy in flight); every wave is done with V(j) ------
+    if (j2 >= 0) wait_vmcnt<0>();
+    lds_barrier();
     if (j2 >= 0) dma_tile<T, D, true>(vh + static_cast<int64_t>(j2) * T * D, vs, wave, lane);
+  };
 
-    j = j2;
-    vk = vk2;
-    n = n2;
+  // Normalise and store the 32 x D rows of this wave (0 for padding query
+  // rows and for rows without keys; NaN when l == 0 or l is NaN).
+  auto store_rows = [&]() {
+    const int64_t ibh = item / num_tiles;
+    const int itile = item - static_cast<int>(ibh) * num_tiles;
+    const int vq = clampi(vbs[itile], 0, T);
+    const int ln = launder(lane);  // per-lane addresses computed here, not hoisted
+    const int row = wave * 32 + (ln & 31);
+    float l_tot;
+    {
+      float lo_half, hi_half;
+      swap_halves(l_run, lo_half, hi_half);
+      l_tot = lo_half + hi_half;
+    }
+    const bool zero_row = !any_keys || row >= vq;
+    const float inv = l_tot != 0.0f ? 1.0f / l_tot : __builtin_nanf("");
+    uint16_t* dst = out + ((ibh * num_tiles + itile) * T + row) * D + 4 * (ln >> 5);
+#pragma unroll
+    for (int db = 0; db < C::kDBlocks; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = zero_row ? 0.0f : acc[db][4 * g + e] * inv;
+        const bf16x2_t lo2 = to_bf16x2(x[0], x[1]);
+        const bf16x2_t hi2 = to_bf16x2(x[2], x[3]);
+        uint2 pkd;
+        pkd.x = __builtin_bit_cast(unsigned, lo2);
+        pkd.y = __builtin_bit_cast(unsigned, hi2);
+        *reinterpret_cast<uint2*>(dst + 32 * db + 8 * g) = pkd;
+      }
+  };
+
+  // The segment in chunks of kThreads list entries; within a chunk the tiles
+  // are pipelined (the copies of the next tile overlap the current one).
+  for (int base = a; base < end; base += C::kThreads) {
+    const int total = compact_list<T, D>(list, base, end, vbs, num_tiles, tl, wave_count, tid,
+                                         wave, lane);
+    if (total == 0) continue;
+    any_keys = true;
+    int2 e = tl[0];
+    const int j0 = __builtin_amdgcn_readfirstlane(e.x);
+    int vk = __builtin_amdgcn_readfirstlane(e.y);
+    // Q must be in registers before the first tile DMA is issued: the DMAs
+    // are invisible to the compiler's wait-count bookkeeping, and an explicit
+    // drain here keeps it from placing waits for Q inside the tile loop.
+    wait_vmcnt<0>();
+    dma_tile<T, D, false>(kh + static_cast<int64_t>(j0) * T * D, ks, wave, lane);
+    dma_tile<T, D, true>(vh + static_cast<int64_t>(j0) * T * D, vs, wave, lane);
+    wait_vmcnt<C::kDmaPerTile>();  // K(j0) has landed (V(j0) may be in flight)
+    lds_barrier();
+    for (int t = 0; t < total; ++t) {
+      int j2 = -1, vk2 = 0;
+      if (t + 1 < total) {
+        e = tl[t + 1];
+        j2 = __builtin_amdgcn_readfirstlane(e.x);
+        vk2 = __builtin_amdgcn_readfirstlane(e.y);
+      }
+      // Tiles with at most half their keys valid take the half-size step.
+      if (vk > T / 2) {
+        tile_step(std::integral_constant<int, T / 32>{}, vk, j2);
+      } else {
+        tile_step(std::integral_constant<int, T / 64>{}, vk, j2);
+      }
+      vk = vk2;
+    }
+  }
+  wait_vmcnt<0>();  // Q, when no tile was processed
+
+  if (nseg == 1) {  // the whole item: store
+    store_rows();
+    return;
   }
 
-  // ---- epilogue ------------------------------------------------------------------
-  float l_tot;
+  // ---- a split item: store this segment's partial; the last segment to arrive
+  //      merges all of them, in segment order, and stores the rows ---------------------
+  const int ln = launder(lane);
   {
-    float a, b;
-    swap_halves(l_run, a, b);
-    l_tot = a + b;
+    float* slot = ws + static_cast<int64_t>(unit2) * S::kFloats;
+#pragma unroll
+    for (int db = 0; db < C::kDBlocks; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *reinterpret_cast<float4*>(slot + (((wave * C::kDBlocks + db) * 4 + r4) * 64 + ln) * 4) =
+            make_float4(acc[db][4 * r4], acc[db][4 * r4 + 1], acc[db][4 * r4 + 2],
+                        acc[db][4 * r4 + 3]);
+    slot[S::kM + wave * 64 + ln] = m_run;
+    slot[S::kL + wave * 64 + ln] = l_run;
+    if (tid == 0) slot[S::kAny] = any_keys ? 1.0f : 0.0f;
   }
-  const bool zero_row = !any_keys || qrow >= vq;
-  const float inv = l_tot != 0.0f ? 1.0f / l_tot : __builtin_nanf("");
-  uint16_t* dst = oh + (static_cast<int64_t>(tile_i) * T + qrow) * D + 4 * half;
+  asm volatile("" ::: "memory");  // the stores above stay above the wait
+  wait_vmcnt<0>();  // this thread's partial stores are complete ...
+  __syncthreads();  // ... and so are everyone's, before the arrival is counted
+  int* counter = counters + (item - n_whole);
+  if (tid == 0) arrival = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (__builtin_amdgcn_readfirstlane(arrival) != nseg - 1) return;
+  asm volatile("" ::: "memory");  // the loads below stay below the arrival
+
+  // last to arrive: reset the counter for the next launch on this stream, merge
+  if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  float mm = -INFINITY;
+  bool any_all = false;
 #pragma unroll
   for (int db = 0; db < C::kDBlocks; ++db)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      float x[4];
+    for (int rr = 0; rr < 16; ++rr) acc[db][rr] = 0.0f;
+  l_run = 0.0f;
+  for (int sg = 0; sg < nseg; ++sg) {
+    const float* slot = ws + static_cast<int64_t>(unit2 - seg + sg) * S::kFloats;
+    const float ms = slot[S::kM + wave * 64 + ln];
+    const float ls = slot[S::kL + wave * 64 + ln];
+    const float as = slot[S::kAny];
+    const float mn = fmaxf(mm, ms);
+    const float mnc = (mn == -INFINITY ? 0.0f : mn) * c;
+    const float sa = __builtin_amdgcn_exp2f(mm * c - mnc);
+    const float sb = __builtin_amdgcn_exp2f(ms * c - mnc);
+    mm = mn;
+    l_run = l_run * sa + ls * sb;
+    any_all = any_all || as != 0.0f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = zero_row ? 0.0f : acc[db][4 * g + e] * inv;
-      const bf16x2_t lo = to_bf16x2(x[0], x[1]);
-      const bf16x2_t hi = to_bf16x2(x[2], x[3]);
-      uint2 pkd;
-      pkd.x = __builtin_bit_cast(unsigned, lo);
-      pkd.y = __builtin_bit_cast(unsigned, hi);
-      *reinterpret_cast<uint2*>(dst + 32 * db + 8 * g) = pkd;
-    }
+    for (int db = 0; db < C::kDBlocks; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const float4 xv = *reinterpret_cast<const float4*>(
+            slot + (((wave * C::kDBlocks + db) * 4 + r4) * 64 + ln) * 4);
+        acc[db][4 * r4 + 0] = acc[db][4 * r4 + 0] * sa + xv.x * sb;
+        acc[db][4 * r4 + 1] = acc[db][4 * r4 + 1] * sa + xv.y * sb;
+        acc[db][4 * r4 + 2] = acc[db][4 * r4 + 2] * sa + xv.z * sb;
+        acc[db][4 * r4 + 3] = acc[db][4 * r4 + 3] * sa + xv.w * sb;
+      }
+  }
+  any_keys = any_all;
+  store_rows();
 }
 
 template <int T, int D>
 hipError_t launch(const bsa::FwdProblem& p, hipStream_t stream) {
   const void* fn = reinterpret_cast<const void*>(&bsa_fwd_kernel<T, D>);
-  dim3 grid(static_cast<unsigned>(p.num_tiles), static_cast<unsigned>(p.batch_heads));
   dim3 block(Cfg<T, D>::kThreads);
   const float c = static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(D))) * kLog2e;
   const uint16_t* q = p.q;
@@ -284,15 +485,53 @@ hipError_t launch(const bsa::FwdProblem& p, hipStream_t stream) {
   const int32_t* vbs = p.block_sizes;
   uint16_t* out = p.out;
   int nt = p.num_tiles, ms = p.max_sel;
-  int items = static_cast<int>(p.batch_heads * p.num_tiles);
+  int n_whole = p.n_whole, n_whole_padded = (p.n_whole + 7) / 8 * 8;
+  int n_split_units = p.n_split_units, splits = p.splits;
+  float* ws = p.ws;
+  int* counters = p.counters;
   float cc = c;
-  void* args[] = {&q, &k, &v, &idx, &num, &vbs, &out, &nt, &ms, &items, &cc};
-  return hipLaunchKernel(fn, grid, block, args, 0, stream);
+  void* args[] = {&q, &k, &v, &idx, &num, &vbs, &out, &nt, &ms, &n_whole, &n_whole_padded,
+                  &n_split_units, &splits, &ws, &counters, &cc};
+  const int units = n_whole_padded + n_split_units;
+  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(units)), block, args, 0, stream);
+}
+
+// Work split.  Workgroups run in rounds of `resident` (occupancy x CUs); the
+// items that fill whole rounds run whole, and when the leftover items would
+// leave the last round less than half full (e.g. 768 items on 512 resident
+// workgroups: 256 left over), each leftover item's list is cut into
+// s = min(4, resident / leftover) segments, so that the last round is full
+// (256 x 2), as long as every segment keeps at least 4 list positions.
+template <int T, int D>
+hipError_t plan(const bsa::FwdProblem& p, bsa::FwdPlan* plan) {
+  int per_cu = 0;
+  const hipError_t err = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      &per_cu, reinterpret_cast<const void*>(&bsa_fwd_kernel<T, D>), Cfg<T, D>::kThreads, 0);
+  if (err != hipSuccess) return err;
+  if (per_cu < 1) per_cu = 1;
+  const int64_t resident = static_cast<int64_t>(per_cu) * p.num_cus;
+  const int64_t items = p.batch_heads * p.num_tiles;
+  const int positions = p.max_sel > 0 ? p.max_sel : 1;
+  const int64_t left = items % resident;
+  int64_t s = left > 0 && 2 * left <= resident ? resident / left : 1;
+  if (s > 4) s = 4;
+  while (s > 1 && positions / s < 4) --s;
+  plan->splits = static_cast<int32_t>(s);
+  plan->n_whole = static_cast<int32_t>(s > 1 ? items - left : items);
+  plan->n_split_units = static_cast<int32_t>(s > 1 ? left * s : 0);
+  plan->ws_bytes = static_cast<size_t>(plan->n_split_units) * Slot<T, D>::kFloats * sizeof(float);
+  plan->counter_bytes = s > 1 ? static_cast<size_t>(left) * sizeof(int) : 0;
+  return hipSuccess;
 }
 
 }  // namespace
 
 namespace bsa {
+
+hipError_t plan_fwd(const FwdProblem& p, FwdPlan* out) {
+  if (p.tile == 128) return p.head_dim == 128 ? plan<128, 128>(p, out) : plan<128, 64>(p, out);
+  return p.head_dim == 128 ? plan<64, 128>(p, out) : plan<64, 64>(p, out);
+}
 
 hipError_t launch_fwd(const FwdProblem& p, hipStream_t stream) {
   if (p.tile == 128) return p.head_dim == 128 ? launch<128, 128>(p, stream)

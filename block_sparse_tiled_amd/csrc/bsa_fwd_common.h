@@ -123,6 +123,18 @@ __device__ __forceinline__ uint32_t launder_s(uint32_t x) {
   return x;
 }
 
+// An opaque copy of x: keeps the compiler from hoisting per-iteration
+// expressions of x out of the tile loop (which costs registers it does not have).
+__device__ __forceinline__ int launder(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+__device__ __forceinline__ float launder_f(float x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // Copy one T x D bf16 tile (rows at stride D from `src`) into `lds`, one
 // 1 KiB block per wave instruction.  The swizzle repeats every kPeriod
 // blocks, so a lane needs at most kPeriod distinct offsets plus a uniform
@@ -133,20 +145,14 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, uint1
   using C = Cfg<T, D>;
   constexpr int kPeriod = kIsV ? 1 : (D == 128 ? 4 : 2);
   const uint32_t base = launder_s(__builtin_amdgcn_readfirstlane(lds_address(lds)) + wave * 1024);
+  const int l = launder(lane);  // offsets recomputed per copy, not held across the tile loop
 #pragma unroll
   for (int it = 0; it < C::kDmaPerTile; ++it) {
     const int blk = it * C::kWaves + wave;
     const uint32_t blk_uniform = static_cast<uint32_t>(blk - blk % kPeriod);
-    dma16(src, dma_offset<D, kIsV>(blk % kPeriod, lane) + blk_uniform * 1024u,
+    dma16(src, dma_offset<D, kIsV>(blk % kPeriod, l) + blk_uniform * 1024u,
           base + it * C::kWaves * 1024);
   }
-}
-
-// An opaque copy of x: keeps the compiler from hoisting per-iteration
-// expressions of x out of the tile loop (which costs registers it does not have).
-__device__ __forceinline__ int launder(int x) {
-  asm volatile("" : "+v"(x));
-  return x;
 }
 
 // Zero the slots of padding rows (row >= vk) that this lane's own DMA wrote.

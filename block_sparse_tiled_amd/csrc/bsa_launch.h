@@ -22,8 +22,25 @@ struct FwdProblem {
   int32_t tile;
   int32_t head_dim;
   int32_t num_cus;  // compute units of the device, for the work mapping
+  // set from FwdPlan by the caller before launch_fwd:
+  int32_t n_whole;        // items [0, n_whole) run whole
+  int32_t n_split_units;  // the other items, `splits` list segments each
+  int32_t splits;
+  float* ws;              // n_split_units partial slots (when splits > 1)
+  int32_t* counters;      // one arrival counter per split item, zero between launches
 };
 
+// How the items are cut into work units, and the workspace that needs (none
+// when no item is split).
+struct FwdPlan {
+  int32_t n_whole;
+  int32_t n_split_units;
+  int32_t splits;
+  size_t ws_bytes;
+  size_t counter_bytes;
+};
+
+hipError_t plan_fwd(const FwdProblem& p, FwdPlan* plan);
 hipError_t launch_fwd(const FwdProblem& p, hipStream_t stream);
 
 struct LayoutProblem {
