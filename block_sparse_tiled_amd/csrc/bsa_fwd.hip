@@ -258,9 +258,11 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
       const int lim = vk - 4 * half;  // register r of block kb holds key 32*kb + 8*(r/4) + r%4 (+4*half)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
+        if (32 * kb + 32 > vk) {  // only the blocks that reach vk (uniform branch)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (32 * kb + 8 * (r >> 2) + (r & 3) >= lim) s[kb][r] = -INFINITY;
+          for (int r = 0; r < 16; ++r)
+            if (32 * kb + 8 * (r >> 2) + (r & 3) >= lim) s[kb][r] = -INFINITY;
+        }
     }
     float mx[NKB];
 #pragma unroll
