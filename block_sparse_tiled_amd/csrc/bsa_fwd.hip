@@ -195,6 +195,8 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   float l_run = 0.0f;       // this half-wave's share of the softmax sum
   bool any_keys = false;
 
+  const DmaLane<T, D, false> k_dma(wave, lane);
+  const DmaLane<T, D, true> v_dma(wave, lane);
   // Loop-invariant parts of the LDS operand addresses.
   const int k_swz = swz_k<D>(col);  // rows 32*kb + col share it
   const int tr_i = lane & 15, tr_g = (lane >> 4) & 1;
@@ -251,7 +253,7 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
       __builtin_amdgcn_sched_barrier(0);  // keeps the reads one step ahead, no further
     }
     lds_barrier();  // every wave is done with K(j)
-    if (j2 >= 0) dma_tile<T, D, false>(kh + static_cast<int64_t>(j2) * T * D, ks, wave, lane);
+    if (j2 >= 0) dma_tile<T, D, false>(kh + static_cast<int64_t>(j2) * T * D, ks, wave, k_dma);
 
     // ---- mask keys at or past vk (whole blocks included), running max ------------
     if (vk < 32 * NKB) {
@@ -335,7 +337,7 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     // ---- K(j2) landed (the only copy in flight); every wave is done with V(j) ------
     if (j2 >= 0) wait_vmcnt<0>();
     lds_barrier();
-    if (j2 >= 0) dma_tile<T, D, true>(vh + static_cast<int64_t>(j2) * T * D, vs, wave, lane);
+    if (j2 >= 0) dma_tile<T, D, true>(vh + static_cast<int64_t>(j2) * T * D, vs, wave, v_dma);
   };
 
   // Normalise and store the 32 x D rows of this wave (0 for padding query
@@ -385,8 +387,8 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     // are invisible to the compiler's wait-count bookkeeping, and an explicit
     // drain here keeps it from placing waits for Q inside the tile loop.
     wait_vmcnt<0>();
-    dma_tile<T, D, false>(kh + static_cast<int64_t>(j0) * T * D, ks, wave, lane);
-    dma_tile<T, D, true>(vh + static_cast<int64_t>(j0) * T * D, vs, wave, lane);
+    dma_tile<T, D, false>(kh + static_cast<int64_t>(j0) * T * D, ks, wave, k_dma);
+    dma_tile<T, D, true>(vh + static_cast<int64_t>(j0) * T * D, vs, wave, v_dma);
     wait_vmcnt<C::kDmaPerTile>();  // K(j0) has landed (V(j0) may be in flight)
     lds_barrier();
     for (int t = 0; t < total; ++t) {

@@ -135,23 +135,37 @@ __device__ __forceinline__ float launder_f(float x) {
   return x;
 }
 
+// Per-lane byte offsets of a wave's tile copies.  Instruction it of wave w
+// fills 1 KiB block blk = it*kWaves + w; its offset is the swizzle phase
+// blk % kPeriod's lane offset plus a uniform block term, and the phases a
+// wave meets repeat every kN instructions, so kN (1 or 2) registers hold all
+// of them.  Computed once per workgroup.
+template <int T, int D, bool kIsV>
+struct DmaLane {
+  static constexpr int kWaves = Cfg<T, D>::kWaves;
+  static constexpr int kPeriod = kIsV ? 1 : (D == 128 ? 4 : 2);
+  static constexpr int kGcd = kWaves % kPeriod == 0 ? kPeriod : (kPeriod % kWaves == 0 ? kWaves : 1);
+  static constexpr int kN = kPeriod / kGcd;
+  uint32_t off[kN];
+  __device__ __forceinline__ DmaLane(int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < kN; ++i) off[i] = dma_offset<D, kIsV>((wave + i * kWaves) % kPeriod, lane);
+  }
+};
+
 // Copy one T x D bf16 tile (rows at stride D from `src`) into `lds`, one
-// 1 KiB block per wave instruction.  The swizzle repeats every kPeriod
-// blocks, so a lane needs at most kPeriod distinct offsets plus a uniform
-// per-block term.
+// 1 KiB block per wave instruction (kDmaPerTile instructions per wave).
 template <int T, int D, bool kIsV>
 __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, uint16_t* lds,
-                                         int wave, int lane) {
+                                         int wave, const DmaLane<T, D, kIsV>& dl) {
   using C = Cfg<T, D>;
-  constexpr int kPeriod = kIsV ? 1 : (D == 128 ? 4 : 2);
+  using DL = DmaLane<T, D, kIsV>;
   const uint32_t base = launder_s(__builtin_amdgcn_readfirstlane(lds_address(lds)) + wave * 1024);
-  const int l = launder(lane);  // offsets recomputed per copy, not held across the tile loop
 #pragma unroll
   for (int it = 0; it < C::kDmaPerTile; ++it) {
     const int blk = it * C::kWaves + wave;
-    const uint32_t blk_uniform = static_cast<uint32_t>(blk - blk % kPeriod);
-    dma16(src, dma_offset<D, kIsV>(blk % kPeriod, l) + blk_uniform * 1024u,
-          base + it * C::kWaves * 1024);
+    const uint32_t blk_uniform = static_cast<uint32_t>(blk - blk % DL::kPeriod);
+    dma16(src, dl.off[it % DL::kN] + blk_uniform * 1024u, base + it * C::kWaves * 1024);
   }
 }
 
