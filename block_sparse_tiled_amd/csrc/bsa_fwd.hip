@@ -4,37 +4,53 @@
 //  - 128-token sm_121a forward commit: the operation, (q, k, v, q2k_idx,
 //    q2k_num, variable_block_sizes) -> out, inference only, no log-sum-exp;
 //  - hardening commit: a NaN softmax sum yields a NaN row (test l != 0, not
-//    l > 0), rows without keys stay zero, V padding rows are zeroed on
-//    partial key chunks and key steps wholly past the valid keys are
-//    skipped, so NaN/Inf padding never reaches the output; its QK/PV overlap
-//    (one tile's loads in flight while another is computed) is realised
-//    here with LDS DMA;
-//  - Attn-QAT commit: full key tiles run without bounds masks and only the
-//    partial tail tile takes the masked step.
+//    l > 0), rows without keys stay zero, and NaN/Inf in padding rows never
+//    reach the output; its QK/PV overlap (one tile's loads in flight while
+//    another is computed) is realised here with LDS DMA;
+//  - Attn-QAT commit: full key tiles run without bounds masks; here only
+//    tiles shorter than T take the mask, and only on the 32-key blocks that
+//    reach the valid length.
+// That commit also skips key steps wholly past the valid keys; this kernel
+// instead runs every tile at full size (masked logits give p = 0 against
+// zeroed V rows, adding exact zeros), which keeps one register assignment
+// for the accumulators across the tile loop.
 //
-// Work mapping.  One workgroup per (batch*head, query tile) with T/32 waves,
-// each wave owning 32 query rows.  Workgroups are renumbered so that each of
-// the 8 XCDs (dispatched round-robin by linear workgroup id) receives a
-// contiguous run of work items, i.e. whole heads: the key tiles a head's
-// lists share then stay in that XCD's L2.
+// Work mapping.  A work unit is one (batch*head, query tile) item, or one
+// list segment of an item: items that fill whole rounds of resident
+// workgroups run whole, and the items left over for a last, mostly empty
+// round are cut into list segments (see plan()).  One workgroup of T/32
+// waves per unit, each wave owning 32 query rows.  Units are renumbered so
+// that each of the 8 XCDs (dispatched round-robin by linear workgroup id)
+// receives a contiguous run, i.e. whole heads: the workgroups of one XCD
+// start together on consecutive query tiles of one head and sweep its key
+// tiles together, so the tiles stay in that XCD's L2.
 //
-// Data movement.  K and V tiles are copied HBM -> LDS with LDS DMA
-// (global_load_lds_dwordx4, 16 bytes per lane, no registers).  Rows are dense
-// in LDS with the 16-byte chunks of each row XOR-swizzled by the row index so
-// that the MFMA operand reads are free of bank conflicts.  One K and one V
-// buffer per workgroup: K(n+1) is requested as soon as every wave has
-// finished reading K(n) and lands during the softmax and P.V of tile n;
-// V(n+1) is requested after P.V(n) and lands during Q.K(n+1).
+// Data movement.  Each list chunk is first compacted into LDS (usable tile
+// indices with their valid lengths).  K and V tiles are copied HBM -> LDS
+// with LDS DMA (global_load_lds_dwordx4, 16 bytes per lane, no registers).
+// Rows are dense in LDS with the 16-byte chunks of each row XOR-swizzled by
+// the row index so that the MFMA operand reads are free of bank conflicts.
+// One K and one V buffer per workgroup (two workgroups share a CU): K(n+1) is
+// requested as soon as every wave has finished reading K(n) and lands during
+// the softmax and P.V of tile n; V(n+1) is requested after P.V(n) and lands
+// during Q.K(n+1).  Three workgroup barriers per tile.
 //
-// Math.  Each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so
-// every lane holds the logits of ONE query (16 keys per 32-key block, the
-// other 16 in lane^32): the row max is an in-lane reduction plus one
-// v_permlane32_swap, and the running sum stays split across the two halves
-// until the end.  The online softmax runs in the exp2 domain with
-// scale*log2(e) folded into one FMA; P is rounded to bf16 once and both the
-// row sum (v_dot2 with ones) and O^T += V^T P^T use those rounded values.
-// V^T operands come straight from the row-major V tile through the LDS
-// transpose read ds_read_b64_tr_b16.
+// Math.  Each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16, k-step
+// outer over independent accumulators, so every lane holds the logits of ONE
+// query (16 keys per 32-key block, the other 16 in lane^32): the row max is
+// an in-lane reduction plus one v_permlane32_swap, and the running sum stays
+// split across the two halves until the end.  The online softmax runs in the
+// exp2 domain with scale*log2(e) folded into one FMA; P is rounded to bf16
+// once and both the row sum (v_dot2 with ones) and O^T += V^T P^T use those
+// rounded values.  V^T operands come straight from the row-major V tile
+// through the LDS transpose read ds_read_b64_tr_b16.  Operand reads run one
+// step ahead of the MFMAs that use them.
+//
+// Split items.  A segment stores its (m, l, unnormalised O) partial in a
+// workspace slot and counts its arrival; the last segment to arrive merges
+// the partials in segment order (the same guarded rescaling as the online
+// update, so the result does not depend on which segment merges) and stores
+// the rows.
 //
 // The MFMA and LDS-transpose register layouts relied on are listed in
 // bsa_fwd_common.h.
@@ -47,8 +63,6 @@
 //   - the final row is 0 without keys, NaN when keys exist but l == 0 (all
 //     logits -inf) or l is NaN, acc / l otherwise; padding query rows are 0.
 #include <hip/hip_runtime.h>
-
-#include <type_traits>
 
 #include "bsa_fwd_common.h"
 #include "bsa_launch.h"
@@ -206,11 +220,11 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   const f32x16_t zero16 = {};
   const float neg_inf = launder_f(-INFINITY);
 
-  // K operands of k-step kk for the blocks below NKB.
+  // K operands of k-step kk for every 32-key block.
   // (the per-lane swizzle is laundered so that the addresses of all k-steps
   // are recomputed per step rather than held in registers across the loop)
-  auto read_k = [&](auto nkb_c, int kk, bf16x8_t* dst) {
-    constexpr int NKB = decltype(nkb_c)::value;
+  auto read_k = [&](int kk, bf16x8_t* dst) {
+    constexpr int NKB = C::kKeyBlocks;
     const int chunk = (2 * kk + half) ^ launder(k_swz);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -230,26 +244,27 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
   };
 
-  // One tile with NKB 32-key blocks holding valid keys.  On entry K(j) is in
-  // LDS and visible, V(j) may be in flight; on exit K(j2) is in LDS and
-  // visible and V(j2) is requested.
-  auto tile_step = [&](auto nkb_c, int vk, int j2) {
-    constexpr int NKB = decltype(nkb_c)::value;
+  // One tile of vk valid keys (1 <= vk <= T).  On entry K(j) is in LDS and
+  // visible, V(j) may be in flight; on exit K(j2) is in LDS and visible and
+  // V(j2) is requested.  Every tile takes the full-size step (all T/32 key
+  // blocks): keys at or past vk are masked, and a single step keeps the
+  // accumulators in one register assignment across the loop (a second,
+  // half-size step made the compiler move all of them every tile).
+  auto tile_step = [&](int vk, int j2) {
+    constexpr int NKB = C::kKeyBlocks;
 
     // ---- S^T = K_j Q^T, k-step outer: NKB independent accumulators, the
     //      operands of step kk + 1 requested before the MFMAs of step kk ----------
     f32x16_t s[NKB];
-    bf16x8_t ka[NKB], kn[NKB];
-    read_k(nkb_c, 0, ka);
+    bf16x8_t kop[2][NKB];  // operands of steps kk (kop[kk & 1]) and kk + 1, no copies
+    read_k(0, kop[0]);
 #pragma unroll
     for (int kk = 0; kk < C::kKSteps; ++kk) {
-      if (kk + 1 < C::kKSteps) read_k(nkb_c, kk + 1, kn);
+      if (kk + 1 < C::kKSteps) read_k(kk + 1, kop[(kk + 1) & 1]);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kb], qop[kk], kk ? s[kb] : zero16, 0,
-                                                        0, 0);
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) ka[kb] = kn[kb];
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk & 1][kb], qop[kk],
+                                                        kk ? s[kb] : zero16, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);  // keeps the reads one step ahead, no further
     }
     lds_barrier();  // every wave is done with K(j)
@@ -306,14 +321,14 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     lds_barrier();
 
     // ---- per 16-key chunk: P = exp2(S*c - m*c) in bf16, row sum, O^T += V^T P^T.
-    //      Both chunks of every block below NKB are processed: keys at or past vk
-    //      have p = 0 and zeroed V rows, so they add exact zeros.  The V operands
-    //      of chunk kc + 1 are requested before the exponentials of chunk kc. ----
-    bf16x8_t va[C::kDBlocks], vn[C::kDBlocks];
-    read_v(0, va);
+    //      Every chunk of the tile is processed: keys at or past vk have p = 0
+    //      and zeroed V rows, so they add exact zeros.  The V operands
+    //      of chunk kc + 1 are requested before the exponentials of chunk kc. -----
+    bf16x8_t vop[2][C::kDBlocks];  // operands of chunks kc (vop[kc & 1]) and kc + 1
+    read_v(0, vop[0]);
 #pragma unroll
     for (int kc = 0; kc < 2 * NKB; ++kc) {
-      if (kc + 1 < 2 * NKB) read_v(kc + 1, vn);
+      if (kc + 1 < 2 * NKB) read_v(kc + 1, vop[(kc + 1) & 1]);
       const int e0 = 8 * (kc & 1);
       bf16x2_t pp[4];
 #pragma unroll
@@ -328,9 +343,7 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
           __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
       for (int db = 0; db < C::kDBlocks; ++db)
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db], pk, acc[db], 0, 0, 0);
-#pragma unroll
-      for (int db = 0; db < C::kDBlocks; ++db) va[db] = vn[db];
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[kc & 1][db], pk, acc[db], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -398,12 +411,7 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         j2 = __builtin_amdgcn_readfirstlane(e.x);
         vk2 = __builtin_amdgcn_readfirstlane(e.y);
       }
-      // Tiles with at most half their keys valid take the half-size step.
-      if (vk > T / 2) {
-        tile_step(std::integral_constant<int, T / 32>{}, vk, j2);
-      } else {
-        tile_step(std::integral_constant<int, T / 64>{}, vk, j2);
-      }
+      tile_step(vk, j2);
       vk = vk2;
     }
   }
