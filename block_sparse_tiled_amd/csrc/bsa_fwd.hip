@@ -257,6 +257,7 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     //      operands of step kk + 1 requested before the MFMAs of step kk ----------
     f32x16_t s[NKB];
     bf16x8_t kop[2][NKB];  // operands of steps kk (kop[kk & 1]) and kk + 1, no copies
+    __builtin_amdgcn_s_setprio(1);  // matrix-core phases take issue priority on the SIMD
     read_k(0, kop[0]);
 #pragma unroll
     for (int kk = 0; kk < C::kKSteps; ++kk) {
@@ -267,6 +268,7 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                                                         kk ? s[kb] : zero16, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);  // keeps the reads one step ahead, no further
     }
+    __builtin_amdgcn_s_setprio(0);
     lds_barrier();  // every wave is done with K(j)
     if (j2 >= 0) dma_tile<T, D, false>(kh + static_cast<int64_t>(j2) * T * D, ks, wave, k_dma);
 
@@ -325,6 +327,7 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     //      and zeroed V rows, so they add exact zeros.  The V operands
     //      of chunk kc + 1 are requested before the exponentials of chunk kc. -----
     bf16x8_t vop[2][C::kDBlocks];  // operands of chunks kc (vop[kc & 1]) and kc + 1
+    __builtin_amdgcn_s_setprio(1);
     read_v(0, vop[0]);
 #pragma unroll
     for (int kc = 0; kc < 2 * NKB; ++kc) {
@@ -346,6 +349,8 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[kc & 1][db], pk, acc[db], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
+
+    __builtin_amdgcn_s_setprio(0);
 
     // ---- K(j2) landed (the only copy in flight); every wave is done with V(j) ------
     if (j2 >= 0) wait_vmcnt<0>();
