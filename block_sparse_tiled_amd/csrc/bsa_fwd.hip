@@ -257,7 +257,6 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     //      operands of step kk + 1 requested before the MFMAs of step kk ----------
     f32x16_t s[NKB];
     bf16x8_t kop[2][NKB];  // operands of steps kk (kop[kk & 1]) and kk + 1, no copies
-    __builtin_amdgcn_s_setprio(1);  // matrix-core phases take issue priority on the SIMD
     read_k(0, kop[0]);
 #pragma unroll
     for (int kk = 0; kk < C::kKSteps; ++kk) {
@@ -268,7 +267,6 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                                                         kk ? s[kb] : zero16, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);  // keeps the reads one step ahead, no further
     }
-    __builtin_amdgcn_s_setprio(0);
     lds_barrier();  // every wave is done with K(j)
     if (j2 >= 0) dma_tile<T, D, false>(kh + static_cast<int64_t>(j2) * T * D, ks, wave, k_dma);
 
@@ -327,6 +325,10 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     //      and zeroed V rows, so they add exact zeros.  The V operands
     //      of chunk kc + 1 are requested before the exponentials of chunk kc. -----
     bf16x8_t vop[2][C::kDBlocks];  // operands of chunks kc (vop[kc & 1]) and kc + 1
+    // The P.V phase (MFMAs and the exponentials) takes issue priority on the
+    // SIMD: two workgroups share each SIMD, and the wave in this phase winning
+    // issue pushes the pair towards anti-phase, one wave's softmax and Q.K
+    // under the other's P.V.  (Priority for Q.K as well measured slower.)
     __builtin_amdgcn_s_setprio(1);
     read_v(0, vop[0]);
 #pragma unroll
