@@ -33,7 +33,8 @@
 // One K and one V buffer per workgroup (two workgroups share a CU): K(n+1) is
 // requested as soon as every wave has finished reading K(n) and lands during
 // the softmax and P.V of tile n; V(n+1) is requested after P.V(n) and lands
-// during Q.K(n+1).  Three workgroup barriers per tile.
+// during Q.K(n+1).  Two workgroup barriers per tile: after Q.K(n) (K(n) free,
+// V(n) landed and visible) and after P.V(n) (V(n) free, K(n+1) visible).
 //
 // Math.  Each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16, k-step
 // outer over independent accumulators, so every lane holds the logits of ONE
@@ -267,7 +268,9 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                                                         kk ? s[kb] : zero16, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);  // keeps the reads one step ahead, no further
     }
-    lds_barrier();  // every wave is done with K(j)
+    wait_vmcnt<0>();  // V(j) (the only copy in flight)
+    if (vk < T) zero_padding_rows<T, D>(vs, vk, wave, lane);
+    lds_barrier();  // every wave is done with K(j); V(j) is visible
     if (j2 >= 0) dma_tile<T, D, false>(kh + static_cast<int64_t>(j2) * T * D, ks, wave, k_dma);
 
     // ---- mask keys at or past vk (whole blocks included), running max ------------
@@ -311,14 +314,6 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
     }
 
-    // ---- V(j) in LDS: wait, blank its padding rows ---------------------------------
-    if (j2 >= 0) {
-      wait_vmcnt<C::kDmaPerTile>();  // K(j2) stays in flight
-    } else {
-      wait_vmcnt<0>();
-    }
-    if (vk < T) zero_padding_rows<T, D>(vs, vk, wave, lane);
-    lds_barrier();
 
     // ---- per 16-key chunk: P = exp2(S*c - m*c) in bf16, row sum, O^T += V^T P^T.
     //      Every chunk of the tile is processed: keys at or past vk have p = 0
