@@ -72,42 +72,6 @@ namespace {
 
 using namespace bsa::detail;
 
-// Copies the usable entries of list[base, base + kThreads) -- in range and
-// with at least one valid key -- into tl[] in list order, with their valid
-// lengths; returns how many there are.  One entry per thread; the order is
-// kept by a wave-level prefix count (mbcnt) plus a per-wave offset.
-template <int T, int D>
-__device__ __forceinline__ int compact_list(const int32_t* __restrict__ list, int base, int count,
-                                            const int32_t* __restrict__ vbs, int num_tiles,
-                                            int2* tl, int* wave_count, int tid, int wave,
-                                            int lane) {
-  using C = Cfg<T, D>;
-  const int e = base + tid;
-  int jj = -1, len = 0;
-  if (e < count) {
-    jj = list[e];
-    if (jj >= 0 && jj < num_tiles) len = clampi(vbs[jj], 0, T);
-  }
-  const bool ok = len > 0;
-  const uint64_t m = __ballot(ok);
-  lds_barrier();  // the previous chunk's readers of tl[] and wave_count[] are done
-  if (lane == 0) wave_count[wave] = __popcll(m);
-  lds_barrier();
-  int off = 0, total = 0;
-#pragma unroll
-  for (int w = 0; w < C::kWaves; ++w) {
-    const int cw = wave_count[w];
-    off += w < wave ? cw : 0;
-    total += cw;
-  }
-  const int pos = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
-                                            __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
-  if (ok) tl[off + pos] = make_int2(jj, len);
-  lds_barrier();
-  (void)lane;
-  return __builtin_amdgcn_readfirstlane(total);
-}
-
 // Partials cross workgroups, and XCDs, through the workspace, which is
 // uncached device memory: plain loads, stores and device-scope atomics on it
 // go to memory and are coherent across the XCDs' separate L2 caches without
@@ -391,8 +355,8 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   // The segment in chunks of kThreads list entries; within a chunk the tiles
   // are pipelined (the copies of the next tile overlap the current one).
   for (int base = a; base < end; base += C::kThreads) {
-    const int total = compact_list<T, D>(list, base, end, vbs, num_tiles, tl, wave_count, tid,
-                                         wave, lane);
+    const int total = compact_list<T, C::kWaves>(list, base, end, vbs, num_tiles, tl, wave_count, tid,
+                                                 wave, lane);
     if (total == 0) continue;
     any_keys = true;
     int2 e = tl[0];

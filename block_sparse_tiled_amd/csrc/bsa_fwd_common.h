@@ -161,11 +161,14 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, uint1
   using C = Cfg<T, D>;
   using DL = DmaLane<T, D, kIsV>;
   const uint32_t base = launder_s(__builtin_amdgcn_readfirstlane(lds_address(lds)) + wave * 1024);
+  // the uniform block term goes into the scalar base address, so the lane
+  // offsets stay the kN registers of dl
 #pragma unroll
   for (int it = 0; it < C::kDmaPerTile; ++it) {
     const int blk = it * C::kWaves + wave;
-    const uint32_t blk_uniform = static_cast<uint32_t>(blk - blk % DL::kPeriod);
-    dma16(src, dl.off[it % DL::kN] + blk_uniform * 1024u, base + it * C::kWaves * 1024);
+    const int blk_uniform = blk - blk % DL::kPeriod;
+    dma16(reinterpret_cast<const char*>(src) + blk_uniform * 1024, dl.off[it % DL::kN],
+          base + it * C::kWaves * 1024);
   }
 }
 
@@ -183,6 +186,41 @@ __device__ __forceinline__ void zero_padding_rows(uint16_t* lds, int vk, int wav
     const int blk = it * C::kWaves + wave;
     if (lane_row >= vk - blk * kRowsPerBlock) slot[blk * 64] = make_uint4(0u, 0u, 0u, 0u);
   }
+}
+
+// Copies the usable entries of list[base, min(base + 64*NW, count)) -- in
+// range and with at least one valid key -- into tl[] in list order, with
+// their valid lengths (clamped to T); returns how many there are (uniform).
+// One entry per thread of an NW-wave workgroup; the order is kept by a
+// wave-level prefix count (mbcnt) plus per-wave offsets.  Three barriers.
+template <int T, int NW>
+__device__ __forceinline__ int compact_list(const int32_t* __restrict__ list, int base, int count,
+                                            const int32_t* __restrict__ vbs, int num_tiles,
+                                            int2* tl, int* wave_count, int tid, int wave,
+                                            int lane) {
+  const int e = base + tid;
+  int jj = -1, len = 0;
+  if (e < count) {
+    jj = list[e];
+    if (jj >= 0 && jj < num_tiles) len = clampi(vbs[jj], 0, T);
+  }
+  const bool ok = len > 0;
+  const uint64_t m = __ballot(ok);
+  lds_barrier();  // the previous chunk's readers of tl[] and wave_count[] are done
+  if (lane == 0) wave_count[wave] = __popcll(m);
+  lds_barrier();
+  int off = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int cw = wave_count[w];
+    off += w < wave ? cw : 0;
+    total += cw;
+  }
+  const int pos = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                            __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
+  if (ok) tl[off + pos] = make_int2(jj, len);
+  lds_barrier();
+  return __builtin_amdgcn_readfirstlane(total);
 }
 
 // Uniform read of one int32 through the scalar cache.  The tile lists and
