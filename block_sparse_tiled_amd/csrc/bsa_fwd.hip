@@ -41,11 +41,13 @@
 // query (16 keys per 32-key block, the other 16 in lane^32): the row max is
 // an in-lane reduction plus one v_permlane32_swap, and the running sum stays
 // split across the two halves until the end.  The online softmax runs in the
-// exp2 domain with scale*log2(e) folded into one FMA; P is rounded to bf16
-// once and both the row sum (v_dot2 with ones) and O^T += V^T P^T use those
-// rounded values.  V^T operands come straight from the row-major V tile
-// through the LDS transpose read ds_read_b64_tr_b16.  Operand reads run one
-// step ahead of the MFMAs that use them.
+// exp2 domain with scale*log2(e) folded into one FMA, and the exponent offset
+// follows the running max lazily (only rises of more than 8 in exp2 units);
+// P is rounded to bf16 for O^T += V^T P^T and the row sum adds the fp32 p.
+// V^T operands come straight from the row-major V tile through the LDS
+// transpose read ds_read_b64_tr_b16.  Operand reads run one step ahead of the
+// MFMAs that use them, and in P.V the exponentials of the next 16-key chunk
+// are interleaved with the MFMAs of the current one.
 //
 // Split items.  A segment stores its (m, l, unnormalised O) partial in a
 // workspace slot and counts its arrival; the last segment to arrive merges
@@ -181,7 +183,6 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   const int tr_i = lane & 15, tr_g = (lane >> 4) & 1;
   const int v_row = 4 * half + (tr_i >> 2);  // + 16*kc (+ 8 for the high half)
   const int v_swz = swz_v<D>(v_row);
-  const bf16x2_t ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
   const f32x16_t zero16 = {};
   const float neg_inf = launder_f(-INFINITY);
 
@@ -239,13 +240,16 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 
     // ---- mask keys at or past vk (whole blocks included), running max ------------
     if (vk < 32 * NKB) {
-      const int lim = vk - 4 * half;  // register r of block kb holds key 32*kb + 8*(r/4) + r%4 (+4*half)
+      // register r of block kb holds key 32*kb + 8*(r/4) + r%4 (+ 4 in the high
+      // half-wave): masked when 8*(r/4) + r%4 >= t = vk - 32*kb - 4*half, a
+      // compare against a small inline constant per register
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
         if (32 * kb + 32 > vk) {  // only the blocks that reach vk (uniform branch)
+          const int t = launder(vk - 32 * kb - 4 * half);
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (32 * kb + 8 * (r >> 2) + (r & 3) >= lim) s[kb][r] = -INFINITY;
+            if (8 * (r >> 2) + (r & 3) >= t) s[kb][r] = -INFINITY;
         }
     }
     float mx[NKB];
@@ -266,10 +270,18 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
       swap_halves(mt, a, b);
       mt = fmaxf(a, b);
     }
+    // The exponent offset m_run follows the running max only when the max
+    // rises by more than kRescaleSlack in exp2 units (or leaves -inf); below
+    // that, p = exp2(s*c - m_run*c) stays under 2^kRescaleSlack, which bf16 P
+    // and the fp32 sums hold, and the accumulators are not rescaled.  The
+    // result is the same quotient.  NaN differences (-inf to -inf, +inf to
+    // +inf) compare false and keep the offset.
     const float m_new = fmaxf(m_run, mt);
-    const float mc = (m_new == -INFINITY ? 0.0f : m_new) * c;
-    const float alpha = __builtin_amdgcn_exp2f(m_run * c - mc);
-    m_run = m_new;
+    const bool raise = (m_new - m_run) * c > kRescaleSlack;
+    const float m_use = raise ? m_new : m_run;
+    const float mc = (m_use == -INFINITY ? 0.0f : m_use) * c;
+    const float alpha = raise ? __builtin_amdgcn_exp2f(m_run * c - mc) : 1.0f;
+    m_run = m_use;
     l_run *= alpha;
     if (__any(alpha != 1.0f)) {
 #pragma unroll
@@ -281,8 +293,13 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 
     // ---- per 16-key chunk: P = exp2(S*c - m*c) in bf16, row sum, O^T += V^T P^T.
     //      Every chunk of the tile is processed: keys at or past vk have p = 0
-    //      and zeroed V rows, so they add exact zeros.  The V operands
-    //      of chunk kc + 1 are requested before the exponentials of chunk kc. -----
+    //      and zeroed V rows, so they add exact zeros.  Software-pipelined: the
+    //      exponentials of chunk kc + 1 and the V operand reads of chunk kc + 1
+    //      are interleaved with the four MFMAs of chunk kc (one MFMA, then two
+    //      LDS reads and up to seven VALU instructions), so that the wave's
+    //      VALU work runs under its own MFMAs.  The row sum adds the fp32 p
+    //      (v_dot2 on the packed bf16 P would occupy the matrix pipe and stall
+    //      behind the MFMAs). -----
     bf16x8_t vop[2][C::kDBlocks];  // operands of chunks kc (vop[kc & 1]) and kc + 1
     // The P.V phase (MFMAs and the exponentials) takes issue priority on the
     // SIMD: two workgroups share each SIMD, and the wave in this phase winning
@@ -290,25 +307,43 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     // under the other's P.V.  (Priority for Q.K as well measured slower.)
     __builtin_amdgcn_s_setprio(1);
     read_v(0, vop[0]);
+    auto make_p = [&](int kc) {
+      const int e0 = 8 * (kc & 1);
+      bf16x2_t pp[4];
+      float ps[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kc >> 1][e0 + 2 * e], c, -mc));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kc >> 1][e0 + 2 * e + 1], c, -mc));
+        pp[e] = to_bf16x2(p0, p1);
+        ps[e] = p0 + p1;
+      }
+      l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+      asm volatile("" : "+v"(l_run));  // this chunk's sum is formed here, not in a chain after the tile
+      return __builtin_shufflevector(
+          __builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
+          __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    bf16x8_t pk = make_p(0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kc = 0; kc < 2 * NKB; ++kc) {
       if (kc + 1 < 2 * NKB) read_v(kc + 1, vop[(kc + 1) & 1]);
-      const int e0 = 8 * (kc & 1);
-      bf16x2_t pp[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pp[e] = to_bf16x2(
-            __builtin_amdgcn_exp2f(__builtin_fmaf(s[kc >> 1][e0 + 2 * e], c, -mc)),
-            __builtin_amdgcn_exp2f(__builtin_fmaf(s[kc >> 1][e0 + 2 * e + 1], c, -mc)));
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(pp[e], ones, l_run, false);
-      }
-      const bf16x8_t pk = __builtin_shufflevector(
-          __builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
-          __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+      bf16x8_t pk_next = pk;
+      if (kc + 1 < 2 * NKB) pk_next = make_p(kc + 1);
 #pragma unroll
       for (int db = 0; db < C::kDBlocks; ++db)
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[kc & 1][db], pk, acc[db], 0, 0, 0);
+      if (kc + 1 < 2 * NKB) {
+#pragma unroll
+        for (int g = 0; g < C::kDBlocks; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+          __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);  // seven VALU
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
+      pk = pk_next;
     }
 
     __builtin_amdgcn_s_setprio(0);

@@ -25,10 +25,14 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
+// Largest rise of the running max, in exp2 units, absorbed without moving the
+// exponent offset (p stays below 2^8 = 256).
+constexpr float kRescaleSlack = 8.0f;
 
 template <int T, int D>
 struct Cfg {
@@ -92,24 +96,23 @@ __device__ __forceinline__ uint32_t dma_offset(int blk, int lane) {
   return static_cast<uint32_t>((row * D + chunk * 8) * 2);
 }
 
-// One LDS DMA instruction: 64 lanes x 16 bytes from gbase + voff into LDS at
-// lds_addr + 16 * lane.  Issued as asm so that the compiler's wait-count pass,
-// which cannot tell this workgroup's K and V buffers apart, does not add
-// full drains before unrelated LDS reads; the kernel waits explicitly.  No
-// memory clobber: the statement is volatile, so it keeps its place between
-// the barriers and fences that order it, and the index lists stay scalar
-// loads.
-__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds_addr) {
-  // M0 carries the LDS address; the compiler's own value of M0 is restored.
-  uint32_t saved;
+// One LDS DMA instruction: buffer_load_dwordx4 ... lds copies 64 lanes x 16
+// bytes from the buffer `srd` at byte offset voff + soff into LDS at
+// m0 + 16 * lane.  The buffer descriptor covers one tile, so an offset
+// outside it reads zeros instead of faulting.  Issued as asm so that the
+// compiler's wait-count pass, which cannot tell this workgroup's K and V
+// buffers apart, does not add full drains before unrelated LDS reads; the
+// kernel waits explicitly.  M0 is an input operand, so the compiler writes it
+// (one s_add per copy) and knows its value; the s_nop is the wait state that
+// a write of M0 needs before an LDS DMA.  No memory clobber: the statement is
+// volatile, so it keeps its place between the barriers and fences that order
+// it, and the index lists stay scalar loads.
+__device__ __forceinline__ void dma16(i32x4_t srd, uint32_t voff, uint32_t soff, uint32_t lds_addr) {
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(voff), "s"(gbase), "s"(lds_addr));
+      "buffer_load_dwordx4 %0, %1, %3 offen lds"
+      :
+      : "v"(voff), "s"(srd), "{m0}"(lds_addr), "s"(soff));
 }
 
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
@@ -136,10 +139,12 @@ __device__ __forceinline__ float launder_f(float x) {
 }
 
 // Per-lane byte offsets of a wave's tile copies.  Instruction it of wave w
-// fills 1 KiB block blk = it*kWaves + w; its offset is the swizzle phase
-// blk % kPeriod's lane offset plus a uniform block term, and the phases a
-// wave meets repeat every kN instructions, so kN (1 or 2) registers hold all
-// of them.  Computed once per workgroup.
+// fills 1 KiB block blk = it*kWaves + w, whose global offset is the lane
+// offset of swizzle phase blk % kPeriod plus (blk - blk % kPeriod) KiB.  Of
+// that block term, it*kWaves KiB is the copy's scalar offset; the remainder,
+// w - phase KiB, depends only on the phase, and the phases a wave meets repeat
+// every kN instructions, so kN (1 or 2) registers hold whole lane offsets.
+// Computed once per workgroup.
 template <int T, int D, bool kIsV>
 struct DmaLane {
   static constexpr int kWaves = Cfg<T, D>::kWaves;
@@ -149,26 +154,33 @@ struct DmaLane {
   uint32_t off[kN];
   __device__ __forceinline__ DmaLane(int wave, int lane) {
 #pragma unroll
-    for (int i = 0; i < kN; ++i) off[i] = dma_offset<D, kIsV>((wave + i * kWaves) % kPeriod, lane);
+    for (int i = 0; i < kN; ++i) {
+      const int phase = (wave + i * kWaves) % kPeriod;
+      off[i] = dma_offset<D, kIsV>(phase, lane) + static_cast<uint32_t>((wave - phase) * 1024);
+    }
   }
 };
 
 // Copy one T x D bf16 tile (rows at stride D from `src`) into `lds`, one
 // 1 KiB block per wave instruction (kDmaPerTile instructions per wave).
+// Instruction it of every wave moves both its global offset and its LDS
+// offset on by it * kWaves KiB, which is the scalar offset of the copy (and
+// added to M0); the rest of each address is a lane register of dl.
+// Buffer descriptor: base address, stride 0, size of one tile in bytes, and
+// the gfx9 word 3 for raw 32-bit data (data format 4 at bit 15).
 template <int T, int D, bool kIsV>
 __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, uint16_t* lds,
                                          int wave, const DmaLane<T, D, kIsV>& dl) {
   using C = Cfg<T, D>;
   using DL = DmaLane<T, D, kIsV>;
   const uint32_t base = launder_s(__builtin_amdgcn_readfirstlane(lds_address(lds)) + wave * 1024);
-  // the uniform block term goes into the scalar base address, so the lane
-  // offsets stay the kN registers of dl
+  const uint64_t g = reinterpret_cast<uintptr_t>(src);
+  const i32x4_t srd = {static_cast<int>(static_cast<uint32_t>(g)),
+                       static_cast<int>(static_cast<uint32_t>(g >> 32)), T * D * 2, 0x00020000};
 #pragma unroll
   for (int it = 0; it < C::kDmaPerTile; ++it) {
-    const int blk = it * C::kWaves + wave;
-    const int blk_uniform = blk - blk % DL::kPeriod;
-    dma16(reinterpret_cast<const char*>(src) + blk_uniform * 1024, dl.off[it % DL::kN],
-          base + it * C::kWaves * 1024);
+    const uint32_t soff = it * C::kWaves * 1024;
+    dma16(srd, dl.off[it % DL::kN], soff, base + soff);
   }
 }
 
@@ -184,7 +196,8 @@ __device__ __forceinline__ void zero_padding_rows(uint16_t* lds, int vk, int wav
 #pragma unroll
   for (int it = 0; it < C::kDmaPerTile; ++it) {
     const int blk = it * C::kWaves + wave;
-    if (lane_row >= vk - blk * kRowsPerBlock) slot[blk * 64] = make_uint4(0u, 0u, 0u, 0u);
+    if (vk < (blk + 1) * kRowsPerBlock && lane_row >= vk - blk * kRowsPerBlock)  // uniform test first
+      slot[blk * 64] = make_uint4(0u, 0u, 0u, 0u);
   }
 }
 

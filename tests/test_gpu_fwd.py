@@ -196,6 +196,21 @@ def test_large_logits_stay_finite(oracle_mod):
 
 
 @pytest.mark.parametrize("T,D", [(64, 64), (128, 128)])
+def test_rising_logit_scale(oracle_mod, T, D):
+    """Key tiles scaled up along the list, so that the running max rises from
+    tile to tile by amounts both below and far above the offset slack of the
+    online softmax (the exponent offset moves only on large rises)."""
+    NT = 12
+    w = gen.random_problem(51, B=1, H=2, D=D, T=T, vbs=[T] * (NT - 1) + [T - 9], counts=NT, MS=NT)
+    w.q[...] = gen.to_bf16_bits(gen.bf16_bits_to_f32(w.q) * 3)
+    for j in range(NT):
+        sl = slice(j * T, (j + 1) * T)
+        w.k[:, :, sl] = gen.to_bf16_bits(gen.bf16_bits_to_f32(w.k[:, :, sl]) * (0.25 + 0.4 * j))
+    ref = oracle_out(oracle_mod, w)
+    compare(run_fwd(w), ref, label=f"rising scale T={T} D={D}")
+
+
+@pytest.mark.parametrize("T,D", [(64, 64), (128, 128)])
 def test_index_handling_probe(oracle_mod, T, D):
     """Q = K = 0 gives uniform weights; V rows of tile j are the one-hot e_(j mod D), so
     the output's non-zero pattern names exactly the listed tiles (bit-exact pattern)."""
