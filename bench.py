@@ -36,7 +36,7 @@ WORKLOAD_NAMES = {
     "dense25": "dense_shape_25pct",
     "tiny": "tiny",
 }
-KERNEL_SOURCES = ["bsa_fwd_common.h", "bsa_fwd.hip", "bsa_layout.hip"]
+KERNEL_SOURCES = ["bsa_fwd_common.h", "bsa_fwd.hip"]
 
 
 def pair_flops(w):
@@ -201,6 +201,27 @@ def main():
     traffic = load_traffic(args.workload)
 
     layout_bytes = 4 * 2 * w.D * (w.B * w.H) * (int(w.vbs.sum()) + w.S)
+
+    # The way back (not part of the step): the attention output gathered from the
+    # tile buffer to token-major order through the token -> tile-row map.
+    src_np = np.asarray(w.tile_src_token, np.int64)
+    tokens = int((src_np >= 0).sum())
+    token_row = np.zeros(tokens, np.int32)
+    token_row[src_np[src_np >= 0]] = np.flatnonzero(src_np >= 0)
+    row_dev = put(token_row)
+    back = [torch.empty((w.B, tokens, w.H, w.D), dtype=torch.bfloat16, device=dev)]
+    for _ in range(3):
+        bsa.tile_unlayout([out], row_dev, w.T, outs=back)
+    un_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    n_un = 20
+    torch.cuda.synchronize()
+    un_ev[0].record(stream)
+    for _ in range(n_un):
+        bsa.tile_unlayout([out], row_dev, w.T, outs=back)
+    un_ev[1].record(stream)
+    torch.cuda.synchronize()
+    unlayout_ms = un_ev[0].elapsed_time(un_ev[1]) / n_un
+    unlayout_bytes = 2 * 2 * w.D * w.B * w.H * tokens + 4 * tokens
     rec = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -229,6 +250,12 @@ def main():
         "layout_ms": round(float(np.mean(lay_ms)), 5),
         "layout_gbs": (round(layout_bytes / (float(np.mean(lay_ms)) * 1e-3) / 1e9, 1)
                        if not args.fwd_only else None),
+        "unlayout": {
+            "kernel": "tile_unlayout_kernel",
+            "what": "attention output, tile buffer -> token-major (timed apart from the step)",
+            "ms": round(unlayout_ms, 5),
+            "gbs": round(unlayout_bytes / (unlayout_ms * 1e-3) / 1e9, 1),
+        },
         "roofline": {
             "bound": "mfma",
             "kernel": "bsa_fwd_kernel",

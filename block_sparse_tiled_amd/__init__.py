@@ -5,11 +5,13 @@ ABI in ``include/bsa.h``); this package only marshals arguments.
 """
 from .api import (  # noqa: F401
     BsaError,
+    cube_tile_map,
     fwd,
     fwd_out_shape,
     load,
     status_string,
     tile_layout,
+    tile_unlayout,
     within_launch_limits,
     within_launch_limits_py,
 )

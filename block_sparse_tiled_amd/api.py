@@ -59,6 +59,14 @@ def load():
     lib.bsa_tile_layout.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp, i32,
                                     i64, i64, i64, i64, i32, vp]
     lib.bsa_tile_layout.restype = ctypes.c_int
+    lib.bsa_tile_unlayout.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp, i32,
+                                      i64, i64, i64, i64, i32, vp]
+    lib.bsa_tile_unlayout.restype = ctypes.c_int
+    lib.bsa_cube_num_tiles.argtypes = [i64, i64, i64, i32, i32, i32]
+    lib.bsa_cube_num_tiles.restype = i64
+    ip = ctypes.POINTER(ctypes.c_int32)
+    lib.bsa_cube_tile_map.argtypes = [i64, i64, i64, i32, i32, i32, i32, ip, ip, ip]
+    lib.bsa_cube_tile_map.restype = ctypes.c_int
     lib.bsa_status_string.argtypes = [ctypes.c_int]
     lib.bsa_status_string.restype = ctypes.c_char_p
     lib.bsa_abi_version.argtypes = []
@@ -204,3 +212,73 @@ def tile_layout(srcs, tile_src_token, tile, outs=None):
         _check(lib.bsa_tile_layout(src_arr, dst_arr, len(srcs), _ptr(tile_src_token), tile,
                                    B, S_tok, H, NT, D, _stream_handle(device)))
     return outs
+
+
+def tile_unlayout(tiled, token_row, tile, tokens=None, outs=None):
+    """Inverse of ``tile_layout``: 1..4 bf16 tile buffers [B, H, NT*tile, D] gathered
+    back to token-major [B, S_tok, H, D].
+
+    ``token_row`` is an int32 cuda tensor [S_tok] naming the tile row of each
+    token (entries outside the buffer give +0 rows).
+    """
+    import torch
+
+    lib = load()
+    tiled = list(tiled)
+    if not 1 <= len(tiled) <= 4:
+        raise ValueError("tile_unlayout takes 1 to 4 tensors")
+    device = tiled[0].device
+    if device.type != "cuda":
+        raise ValueError("bsa.tile_unlayout runs on a GPU")
+    for n, x in enumerate(tiled):
+        _require(x, f"tiled[{n}]", torch.bfloat16, device, 4)
+        if x.shape != tiled[0].shape:
+            raise ValueError("all tile buffers must share one shape")
+    _require(token_row, "token_row", torch.int32, device, 1)
+    B, H, rows, D = tiled[0].shape
+    if tile not in TILES or rows % tile:
+        raise ValueError("the tile buffers must hold a whole number of 64- or 128-row tiles")
+    S_tok = token_row.shape[0] if tokens is None else tokens
+    if token_row.shape[0] != S_tok:
+        raise ValueError("token_row must have one entry per token")
+    if outs is None:
+        outs = [torch.empty((B, S_tok, H, D), dtype=torch.bfloat16, device=device) for _ in tiled]
+    else:
+        outs = list(outs)
+        if len(outs) != len(tiled):
+            raise ValueError("one output per input")
+        for n, o in enumerate(outs):
+            _require(o, f"out[{n}]", torch.bfloat16, device, 4)
+            if tuple(o.shape) != (B, S_tok, H, D):
+                raise ValueError("outputs must be [B, S_tok, H, D]")
+    src_arr = (ctypes.c_void_p * len(tiled))(*[_ptr(x) for x in tiled])
+    dst_arr = (ctypes.c_void_p * len(outs))(*[_ptr(o) for o in outs])
+    with torch.cuda.device(device):
+        _check(lib.bsa_tile_unlayout(src_arr, dst_arr, len(tiled), _ptr(token_row), tile,
+                                     B, S_tok, H, rows // tile, D, _stream_handle(device)))
+    return outs
+
+
+def cube_tile_map(latent, cube):
+    """Maps of a video latent (t, h, w) tiled into cubes (ct, ch, cw), computed by the library
+    on the host.
+
+    Returns numpy int32 arrays ``(block_sizes [NT], tile_src_token [NT*tile],
+    token_row [t*h*w])`` with tile = ct*ch*cw.
+    """
+    import numpy as np
+
+    lib = load()
+    t, h, w = (int(x) for x in latent)
+    ct, ch, cw = (int(x) for x in cube)
+    tile = ct * ch * cw
+    nt = lib.bsa_cube_num_tiles(t, h, w, ct, ch, cw)
+    if nt < 0:
+        raise BsaError(1, f"invalid latent {latent} or cube {cube}")
+    vbs = np.empty(nt, np.int32)
+    src = np.empty(nt * tile, np.int32)
+    row = np.empty(t * h * w, np.int32)
+    ip = ctypes.POINTER(ctypes.c_int32)
+    _check(lib.bsa_cube_tile_map(t, h, w, ct, ch, cw, tile, vbs.ctypes.data_as(ip),
+                                 src.ctypes.data_as(ip), row.ctypes.data_as(ip)))
+    return vbs, src, row

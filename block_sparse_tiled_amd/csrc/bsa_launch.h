@@ -57,4 +57,8 @@ struct LayoutProblem {
 
 hipError_t launch_tile_layout(const LayoutProblem& p, hipStream_t stream);
 
+// The inverse gather: p.src are tile buffers, p.dst token-major outputs, and
+// p.tile_src_token holds the tile row of every token (token_row).
+hipError_t launch_tile_unlayout(const LayoutProblem& p, hipStream_t stream);
+
 }  // namespace bsa

@@ -8,6 +8,9 @@
 // permutation and lets every output byte be written exactly once, so padding
 // rows need no separate clearing pass.
 //
+// The inverse gather (tile buffer -> token-major, for the attention output)
+// uses the token -> tile-row map and is written the same way.
+//
 // Pure HBM streaming: each thread moves one 16-byte chunk of a row for every
 // tensor, reading the map entry once.  A workgroup covers whole rows, so the
 // reads of one source row (D*2 contiguous bytes) and the writes of one tile
@@ -54,6 +57,40 @@ __global__ __launch_bounds__(256) void tile_layout_kernel(Ptrs p, int n_tensors,
   }
 }
 
+// The inverse: token-major rows gathered from the tile buffer through the
+// token -> tile-row map.  One 16-byte chunk per thread, chunk index fastest,
+// then head, then token, so the writes of consecutive threads are contiguous
+// and each thread group of D8 threads reads one whole tile row.
+template <int D8>
+__global__ __launch_bounds__(256) void tile_unlayout_kernel(Ptrs p, int n_tensors,
+                                                            const int32_t* __restrict__ token_row,
+                                                            int64_t tokens, int64_t heads,
+                                                            int64_t rows_per_head) {
+  const int64_t b = blockIdx.y;
+  const int64_t chunks = tokens * heads * D8;  // per batch
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; c < chunks;
+       c += stride) {
+    const int ch = static_cast<int>(c % D8);
+    const int64_t th = c / D8;  // token * heads + head
+    const int64_t n = th / heads;
+    const int64_t h = th - n * heads;
+    const int32_t r = token_row[n];
+    const int64_t out_off = b * chunks + c;
+    if (r >= 0 && r < rows_per_head) {
+      const int64_t in_off = ((b * heads + h) * rows_per_head + r) * D8 + ch;
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+        if (x < n_tensors) p.dst[x][out_off] = p.src[x][in_off];
+    } else {
+      const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+        if (x < n_tensors) p.dst[x][out_off] = zero;
+    }
+  }
+}
+
 }  // namespace
 
 namespace bsa {
@@ -76,6 +113,26 @@ hipError_t launch_tile_layout(const LayoutProblem& lp, hipStream_t stream) {
   void* args[] = {&p, &n, &map, &tokens, &heads, &rows};
   const void* fn = d8 == 16 ? reinterpret_cast<const void*>(&tile_layout_kernel<16>)
                             : reinterpret_cast<const void*>(&tile_layout_kernel<8>);
+  return hipLaunchKernel(fn, grid, block, args, 0, stream);
+}
+
+hipError_t launch_tile_unlayout(const LayoutProblem& lp, hipStream_t stream) {
+  Ptrs p;
+  for (int x = 0; x < 4; ++x) {
+    p.src[x] = static_cast<const uint4*>(lp.src[x]);
+    p.dst[x] = static_cast<uint4*>(lp.dst[x]);
+  }
+  const int d8 = lp.head_dim / 8;
+  const int64_t chunks = lp.tokens * lp.heads * d8;
+  const int64_t want = (chunks + 255) / 256;
+  dim3 grid(static_cast<unsigned>(want < 65536 ? want : 65536), static_cast<unsigned>(lp.batch));
+  dim3 block(256);
+  int n = lp.n_tensors;
+  const int32_t* map = lp.tile_src_token;
+  int64_t tokens = lp.tokens, heads = lp.heads, rows = lp.rows_per_head;
+  void* args[] = {&p, &n, &map, &tokens, &heads, &rows};
+  const void* fn = d8 == 16 ? reinterpret_cast<const void*>(&tile_unlayout_kernel<16>)
+                            : reinterpret_cast<const void*>(&tile_unlayout_kernel<8>);
   return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 

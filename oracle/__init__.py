@@ -4,8 +4,7 @@ TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package.  The GPU library
 shares no code with it and never falls back to it.
 
-Two functions are defined here, each following the FastVideo fastvideo-kernel
-commit list (page 3):
+The functions here follow the FastVideo fastvideo-kernel commit list (page 3):
 
 * ``fwd`` / ``fwd_rows`` -- block-sparse softmax attention, the plain
   definition written out in ``bsa_oracle.c`` (binary32, as the pages' kernel
@@ -16,6 +15,13 @@ commit list (page 3):
   and the gate into the tile buffer in B*H*S*D order, written as the gather it
   is equivalent to: output row t of head h reads token ``tile_src_token[t]`` of
   that head, and a row whose source is -1 is padding and holds +0.
+* ``tile_unlayout`` -- the way back from the tile buffer to token-major order
+  after attention: token n of head h reads tile row ``token_row[n]``.
+* ``cube_tile_map`` -- the tiling of a video latent into 3D cubes that the
+  layout step applies (the pages name the scatter into tiles but not the cube
+  shape; the cube is an argument, and the plainest order is taken: cubes
+  row-major over the cube grid, tokens row-major inside a cube, padding rows
+  last).
 
 Parity pins for both live in ``tests/test_oracle_pins.py``.
 """
@@ -154,3 +160,55 @@ def tile_layout(srcs, tile_src_token, tile):
         out[:, :, valid, :] = np.transpose(x[:, tile_src_token[valid], :, :], (0, 2, 1, 3))
         outs.append(out)
     return outs
+
+
+def tile_unlayout(tiled, token_row):
+    """Gather [B, H, NT*T, D] tile buffers back to token-major [B, S_tok, H, D].
+
+    Token n of head h reads tile row ``token_row[n]``; an entry outside the
+    buffer gives a +0 row.  Values are moved bit for bit.
+    """
+    token_row = np.asarray(token_row, dtype=np.int64)
+    outs = []
+    for x in tiled:
+        x = np.asarray(x)
+        B, H, rows, D = x.shape
+        out = np.zeros((B, token_row.size, H, D), dtype=x.dtype)
+        ok = (token_row >= 0) & (token_row < rows)
+        # out[b, n, h, :] = x[b, h, token_row[n], :] for every token n with a row
+        out[:, ok, :, :] = np.transpose(x[:, :, token_row[ok], :], (0, 2, 1, 3))
+        outs.append(out)
+    return outs
+
+
+def cube_tile_map(latent, cube):
+    """Tiling of a t x h x w video latent (token (z*h + y)*w + x) into ct x ch x cw cubes.
+
+    Returns ``(block_sizes [NT], tile_src_token [NT*T], token_row [t*h*w])``
+    with T = ct*ch*cw and NT = ceil(t/ct)*ceil(h/ch)*ceil(w/cw).  Written per
+    token: a token's cube is its coordinates divided by the cube, the cube
+    index runs row-major over the cube grid, and its row inside the tile is its
+    row-major rank within the cube's (edge-clipped) extent.
+    """
+    t, h, w = (int(x) for x in latent)
+    ct, ch, cw = (int(x) for x in cube)
+    tile = ct * ch * cw
+    gz, gy, gx = -(-t // ct), -(-h // ch), -(-w // cw)
+    n_tiles = gz * gy * gx
+    block_sizes = np.zeros(n_tiles, np.int32)
+    tile_src_token = np.full(n_tiles * tile, -1, np.int32)
+    token_row = np.zeros(t * h * w, np.int32)
+    for z in range(t):
+        for y in range(h):
+            for x in range(w):
+                cz, cy, cx = z // ct, y // ch, x // cw
+                c = (cz * gy + cy) * gx + cx
+                ez = min(ct, t - cz * ct)  # extent of this cube after the edge cut
+                ey = min(ch, h - cy * ch)
+                ex = min(cw, w - cx * cw)
+                rank = ((z - cz * ct) * ey + (y - cy * ch)) * ex + (x - cx * cw)
+                token = (z * h + y) * w + x
+                token_row[token] = c * tile + rank
+                tile_src_token[c * tile + rank] = token
+                block_sizes[c] = ez * ey * ex
+    return block_sizes, tile_src_token, token_row

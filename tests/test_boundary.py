@@ -129,6 +129,7 @@ def test_without_a_device_launches_fail_cleanly(lib):
     assert fwd_call(lib) == NO_DEVICE
     arr = (ctypes.c_void_p * 1)(FAKE)
     assert lib.bsa_tile_layout(arr, arr, 1, FAKE, 64, 1, 64, 1, 1, 64, NUL) == NO_DEVICE
+    assert lib.bsa_tile_unlayout(arr, arr, 1, FAKE, 64, 1, 64, 1, 1, 64, NUL) == NO_DEVICE
     import torch
 
     # a CPU tensor is refused: there is no CPU implementation to fall back on
