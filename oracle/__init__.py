@@ -17,6 +17,9 @@ The functions here follow the FastVideo fastvideo-kernel commit list (page 3):
   that head, and a row whose source is -1 is padding and holds +0.
 * ``tile_unlayout`` -- the way back from the tile buffer to token-major order
   after attention: token n of head h reads tile row ``token_row[n]``.
+* ``fwd64`` / ``bwd`` (module ``bsa_bwd``) -- the same forward in fp64 with
+  its log-sum-exp, and its gradients dq, dk, dv (the pages' LSE-requiring
+  autograd path; formulas in that module's docstring).
 * ``cube_tile_map`` -- the tiling of a video latent into 3D cubes that the
   layout step applies (the pages name the scatter into tiles but not the cube
   shape; the cube is an argument, and the plainest order is taken: cubes
@@ -212,3 +215,6 @@ def cube_tile_map(latent, cube):
                 tile_src_token[c * tile + rank] = token
                 block_sizes[c] = ez * ey * ex
     return block_sizes, tile_src_token, token_row
+
+
+from .bsa_bwd import bwd, fwd64  # noqa: E402,F401
