@@ -5,8 +5,11 @@ ABI in ``include/bsa.h``); this package only marshals arguments.
 """
 from .api import (  # noqa: F401
     BsaError,
+    bwd,
+    bwd_k2q,
     cube_tile_map,
     fwd,
+    fwd_lse,
     fwd_out_shape,
     load,
     status_string,

@@ -59,6 +59,12 @@ def load():
     lib.bsa_tile_layout.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp, i32,
                                     i64, i64, i64, i64, i32, vp]
     lib.bsa_tile_layout.restype = ctypes.c_int
+    lib.bsa_fwd_lse.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, i64, i64, i64, i32, i32, vp]
+    lib.bsa_fwd_lse.restype = ctypes.c_int
+    lib.bsa_bwd_k2q.argtypes = [vp, vp, i64, i64, i64, i32, vp, vp, i32, vp]
+    lib.bsa_bwd_k2q.restype = ctypes.c_int
+    lib.bsa_bwd.argtypes = [vp] * 11 + [i32] + [vp] * 4 + [i64, i64, i64, i32, i32, i32, vp]
+    lib.bsa_bwd.restype = ctypes.c_int
     lib.bsa_tile_unlayout.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp, i32,
                                       i64, i64, i64, i64, i32, vp]
     lib.bsa_tile_unlayout.restype = ctypes.c_int
@@ -282,3 +288,104 @@ def cube_tile_map(latent, cube):
     _check(lib.bsa_cube_tile_map(t, h, w, ct, ch, cw, tile, vbs.ctypes.data_as(ip),
                                  src.ctypes.data_as(ip), row.ctypes.data_as(ip)))
     return vbs, src, row
+
+
+def _fwd_args(q, k, v, q2k_idx, q2k_num, block_sizes, tile):
+    import torch
+
+    device = q.device
+    if device.type != "cuda":
+        raise ValueError("block-sparse attention runs on a GPU: q must be a cuda tensor")
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, name, torch.bfloat16, device, 4)
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k and v must have the same shape")
+    B, H, S, D = q.shape
+    if tile not in TILES:
+        raise ValueError(f"tile must be 64 or 128, got {tile}")
+    if S % tile:
+        raise ValueError(f"sequence length {S} is not a multiple of the tile {tile}")
+    NT = S // tile
+    _require(q2k_idx, "q2k_idx", torch.int32, device, 4)
+    _require(q2k_num, "q2k_num", torch.int32, device, 3)
+    _require(block_sizes, "block_sizes", torch.int32, device, 1)
+    if tuple(q2k_idx.shape[:3]) != (B, H, NT) or tuple(q2k_num.shape) != (B, H, NT):
+        raise ValueError("q2k_idx must be [B, H, NT, MS] and q2k_num [B, H, NT]")
+    if tuple(block_sizes.shape) != (NT,):
+        raise ValueError("block_sizes must be [NT]")
+    return device, B, H, S, D, NT
+
+
+def fwd_lse(q, k, v, q2k_idx, q2k_num, block_sizes, tile, out=None, lse=None):
+    """``fwd`` that also returns each row's log-sum-exp (float32 [B, H, NT*tile])."""
+    import torch
+
+    lib = load()
+    device, B, H, S, D, NT = _fwd_args(q, k, v, q2k_idx, q2k_num, block_sizes, tile)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=device) if lse is None else lse
+    _require(out, "out", torch.bfloat16, device, 4)
+    _require(lse, "lse", torch.float32, device, 3)
+    if out.shape != q.shape or tuple(lse.shape) != (B, H, S):
+        raise ValueError("out must have q's shape and lse [B, H, S]")
+    with torch.cuda.device(device):
+        _check(lib.bsa_fwd_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(q2k_idx), _ptr(q2k_num),
+                               _ptr(block_sizes), tile, _ptr(out), _ptr(lse), B, H, NT, D,
+                               int(q2k_idx.shape[3]), _stream_handle(device)))
+    return out, lse
+
+
+def bwd_k2q(q2k_idx, q2k_num, max_k=None):
+    """Transposed tile lists for the backward: (k2q_idx int32 [B, H, NT, max_k],
+    k2q_num int32 [B, H, NT] with the true lengths).  max_k defaults to NT, enough
+    whenever the forward lists hold distinct tiles."""
+    import torch
+
+    lib = load()
+    device = q2k_num.device
+    _require(q2k_idx, "q2k_idx", torch.int32, device, 4)
+    _require(q2k_num, "q2k_num", torch.int32, device, 3)
+    B, H, NT, MS = q2k_idx.shape
+    max_k = NT if max_k is None else int(max_k)
+    k2q_idx = torch.empty((B, H, NT, max_k), dtype=torch.int32, device=device)
+    k2q_num = torch.empty((B, H, NT), dtype=torch.int32, device=device)
+    with torch.cuda.device(device):
+        _check(lib.bsa_bwd_k2q(_ptr(q2k_idx), _ptr(q2k_num), B, H, NT, MS, _ptr(k2q_idx),
+                               _ptr(k2q_num), max_k, _stream_handle(device)))
+    return k2q_idx, k2q_num
+
+
+def bwd(q, k, v, out, dout, lse, q2k_idx, q2k_num, k2q_idx, k2q_num, block_sizes, tile,
+        dq=None, dk=None, dv=None):
+    """Gradients (dq, dk, dv), bf16 like q, of the block-sparse forward for the upstream
+    gradient ``dout``; ``out`` and ``lse`` come from ``fwd_lse``, the transposed lists
+    from ``bwd_k2q``."""
+    import torch
+
+    lib = load()
+    device, B, H, S, D, NT = _fwd_args(q, k, v, q2k_idx, q2k_num, block_sizes, tile)
+    for t, name in ((out, "out"), (dout, "dout")):
+        _require(t, name, torch.bfloat16, device, 4)
+        if t.shape != q.shape:
+            raise ValueError(f"{name} must have q's shape")
+    _require(lse, "lse", torch.float32, device, 3)
+    _require(k2q_idx, "k2q_idx", torch.int32, device, 4)
+    _require(k2q_num, "k2q_num", torch.int32, device, 3)
+    if tuple(lse.shape) != (B, H, S) or tuple(k2q_idx.shape[:3]) != (B, H, NT) or \
+            tuple(k2q_num.shape) != (B, H, NT):
+        raise ValueError("lse must be [B, H, S], k2q_idx [B, H, NT, MK] and k2q_num [B, H, NT]")
+    grads = []
+    for g, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        g = torch.empty_like(q) if g is None else g
+        _require(g, name, torch.bfloat16, device, 4)
+        if g.shape != q.shape:
+            raise ValueError(f"{name} must have q's shape")
+        grads.append(g)
+    delta = torch.empty((B, H, S), dtype=torch.float32, device=device)
+    with torch.cuda.device(device):
+        _check(lib.bsa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+                           _ptr(q2k_idx), _ptr(q2k_num), _ptr(k2q_idx), _ptr(k2q_num),
+                           _ptr(block_sizes), tile, _ptr(grads[0]), _ptr(grads[1]),
+                           _ptr(grads[2]), _ptr(delta), B, H, NT, D, int(q2k_idx.shape[3]),
+                           int(k2q_idx.shape[3]), _stream_handle(device)))
+    return tuple(grads)

@@ -1,0 +1,464 @@
+// Block-sparse tiled attention backward for gfx950 (AMD Instinct MI355X).
+//
+// FastVideo fastvideo-kernel commit list, page 3: the 128-token sm_121a
+// forward commit keeps its binding inference-only because another route's
+// log-sum-exp output feeds an autograd path; the Attn-QAT commit describes a
+// backward of 64x128 dQ and dK/dV tiles.  The pages print no backward
+// formulas; these kernels compute the gradients of the plain forward
+// definition (softmax over the listed tiles' valid keys), per query row r:
+//   P = exp(scale * q_r K^T - lse_r),  dP = dO_r V^T,  D_r = dO_r . out_r,
+//   dS = P * (dP - D_r),  dq_r = scale * dS K,  dK += scale * dS^T q_r,
+//   dV += P^T dO_r.
+//
+// Kernels (all bf16 MFMA 32x32x16 with fp32 accumulation, operands staged in
+// LDS by LDS DMA with the forward's K-tile swizzle):
+//   - k2q_kernel: the transposed lists (for each key tile, the query tiles
+//     whose lists name it, ascending, a tile listed twice appearing twice),
+//     built deterministically: one wave per key tile scans the lists in
+//     order with a ballot-ordered append.
+//   - delta_kernel: D_r = dO_r . out_r in fp32 (0 for padding rows).
+//   - dq_kernel: one workgroup per query tile, T/32 waves of 32 query rows;
+//     per listed key tile, in halves of 64 keys: S^T = K Q^T, P^T, dP^T =
+//     V dO^T, dS^T, then dQ^T += K^T dS^T (the K^T operand through the LDS
+//     transpose read).  Q and dO stay in registers as B operands.
+//   - dkv_kernel: one workgroup per key tile, T/32 waves of 32 key rows;
+//     per query tile of its transposed list, in blocks of 32 queries: S =
+//     Q K^T, P, dP = dO V^T, dS, then dV^T += dO^T P and dK^T += Q^T dS (dO^T
+//     and Q^T through the LDS transpose read).  K and V stay in registers.
+//   The C-layout-to-B-operand reuse and the key (query) order within a
+//   16-wide chunk are those of the forward (bsa_fwd_common.h).
+//
+// Padding and special values: padding key rows (K, V) and padding query rows
+// (Q, dO) are zeroed in LDS after their copy lands, so NaN or Inf there never
+// meets a zero weight; padding query rows get P = 0 in dkv_kernel (their
+// staged lse is +inf); rows without keys have no tiles in dq_kernel and appear
+// in no transposed list; every gradient row of a padding token is written +0.
+// A row whose softmax sum is NaN (lse NaN, or -inf with keys present)
+// propagates NaN, as the plain formula does.
+#include <hip/hip_runtime.h>
+
+#include "bsa_fwd_common.h"
+#include "bsa_launch.h"
+
+namespace {
+
+using namespace bsa::detail;
+
+// ---- transposed lists ---------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k2q_kernel(const int32_t* __restrict__ q2k_idx,
+                                                  const int32_t* __restrict__ q2k_num,
+                                                  int num_tiles, int max_sel, int64_t n_lists,
+                                                  int32_t* __restrict__ k2q_idx,
+                                                  int32_t* __restrict__ k2q_num, int max_k) {
+  const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (wid >= n_lists) return;  // whole waves leave together
+  const int64_t bh = wid / num_tiles;
+  const int j = static_cast<int>(wid - bh * num_tiles);
+  const int32_t* idx_h = q2k_idx + bh * num_tiles * static_cast<int64_t>(max_sel);
+  const int32_t* num_h = q2k_num + bh * num_tiles;
+  int32_t* dst = k2q_idx + wid * max_k;
+  int count = 0;
+  for (int i = 0; i < num_tiles; ++i) {
+    const int n = max_sel > 0 ? clampi(num_h[i], 0, max_sel) : 0;
+    for (int base = 0; base < n; base += 64) {
+      const int e = base + lane;
+      const bool hit = e < n && idx_h[static_cast<int64_t>(i) * max_sel + e] == j;
+      const uint64_t m = __ballot(hit);
+      if (hit) {
+        const int pos = count + __builtin_amdgcn_mbcnt_hi(
+                                    static_cast<uint32_t>(m >> 32),
+                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
+        if (pos < max_k) dst[pos] = i;
+      }
+      count += __popcll(m);
+    }
+  }
+  if (lane == 0) k2q_num[wid] = count;  // the true count (the list holds the first max_k)
+}
+
+// ---- D = rowsum(dO * out) -----------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void delta_kernel(const uint16_t* __restrict__ out,
+                                                    const uint16_t* __restrict__ dout,
+                                                    const int32_t* __restrict__ vbs, int num_tiles,
+                                                    int tile, int64_t rows,
+                                                    float* __restrict__ delta) {
+  constexpr int kLanes = D / 8;  // lanes per row, 8 bf16 each
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t row = gid / kLanes;
+  const int part = static_cast<int>(gid % kLanes);
+  float acc = 0.0f;
+  bool valid = false;
+  if (row < rows) {
+    const int64_t r = row % (static_cast<int64_t>(num_tiles) * tile);
+    const int t = static_cast<int>(r / tile);
+    valid = static_cast<int>(r % tile) < clampi(vbs[t], 0, tile);
+    if (valid) {
+      const uint4 o = *reinterpret_cast<const uint4*>(out + row * D + 8 * part);
+      const uint4 g = *reinterpret_cast<const uint4*>(dout + row * D + 8 * part);
+      const uint32_t ow[4] = {o.x, o.y, o.z, o.w}, gw[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        acc += __uint_as_float(ow[x] << 16) * __uint_as_float(gw[x] << 16);
+        acc += __uint_as_float(ow[x] & 0xffff0000u) * __uint_as_float(gw[x] & 0xffff0000u);
+      }
+    }
+  }
+#pragma unroll
+  for (int off = kLanes / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  if (row < rows && part == 0) delta[row] = valid ? acc : 0.0f;
+}
+
+// ---- LDS operand reads shared by the two gradient kernels --------------------------------
+// A operand (32 rows x 16 of the D axis) from rows [row0, row0 + 32) of a
+// K-swizzled tile: lane l reads row row0 + l % 32, columns 16*kk + 8*half ..
+template <int D>
+__device__ __forceinline__ bf16x8_t read_rows(const uint16_t* tile, int row0, int kk, int col,
+                                              int half) {
+  const int row = row0 + col;
+  const int chunk = (2 * kk + half) ^ swz_k<D>(row);
+  return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(tile + row * D + 8 * chunk));
+}
+
+// A operand (32 of the D axis x 16 rows) = the transpose of rows [16c, 16c + 16)
+// of a K-swizzled tile, columns 32*db .. 32*db + 31, rows in the forward's
+// order within a 16-wide chunk (element e of half h is row 8*(e/4) + 4*h + e%4).
+template <int D>
+__device__ __forceinline__ bf16x8_t read_rows_t(const uint16_t* tile, int c, int db, int lane) {
+  const int tr_i = lane & 15, tr_g = (lane >> 4) & 1, half = lane >> 5;
+  const int row_lo = 16 * c + 4 * half + (tr_i >> 2);
+  const int row_hi = row_lo + 8;
+  const int colv = 32 * db + 16 * tr_g + 4 * (tr_i & 3);
+  const int off_lo = ((colv >> 3) ^ swz_k<D>(row_lo)) * 8 + (colv & 7);
+  const int off_hi = ((colv >> 3) ^ swz_k<D>(row_hi)) * 8 + (colv & 7);
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(tile + row_lo * D + off_lo));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(tile + row_hi * D + off_hi));
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// bf16 B operand from eight fp32 values of an accumulator (registers e0 .. e0+7).
+__device__ __forceinline__ bf16x8_t pack8(const f32x16_t& x, int e0) {
+  const bf16x2_t a = to_bf16x2(x[e0 + 0], x[e0 + 1]);
+  const bf16x2_t b = to_bf16x2(x[e0 + 2], x[e0 + 3]);
+  const bf16x2_t c = to_bf16x2(x[e0 + 4], x[e0 + 5]);
+  const bf16x2_t d = to_bf16x2(x[e0 + 6], x[e0 + 7]);
+  return __builtin_shufflevector(__builtin_shufflevector(a, b, 0, 1, 2, 3),
+                                 __builtin_shufflevector(c, d, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Store a D^T x 32 accumulator set (lane = row col, register r of block db =
+// column 32*db + 8*(r/4) + 4*half + r%4) as bf16 rows, times `mul`; +0 rows
+// where `zero`.
+template <int D>
+__device__ __forceinline__ void store_t(uint16_t* dst_row, const f32x16_t* acc, float mul,
+                                        bool zero, int half) {
+  constexpr int NDB = D / 32;
+  uint16_t* dst = dst_row + 4 * half;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = zero ? 0.0f : acc[db][4 * g + e] * mul;
+      uint2 pk;
+      pk.x = __builtin_bit_cast(unsigned, to_bf16x2(x[0], x[1]));
+      pk.y = __builtin_bit_cast(unsigned, to_bf16x2(x[2], x[3]));
+      *reinterpret_cast<uint2*>(dst + 32 * db + 8 * g) = pk;
+    }
+}
+
+// Work item of linear workgroup id L (whole set only), XCD-aware as in the
+// forward: XCD x = L % 8 receives a contiguous run of items.
+__device__ __forceinline__ int item_of(int L, int n_padded) {
+  return (L & 7) * (n_padded >> 3) + (L >> 3);
+}
+
+// ---- dQ -----------------------------------------------------------------------------------
+template <int T, int D>
+__global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(2, T == 128 ? 2 : 4)))
+void dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+               const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+               const float* __restrict__ lse, const float* __restrict__ delta,
+               const int32_t* __restrict__ q2k_idx, const int32_t* __restrict__ q2k_num,
+               const int32_t* __restrict__ vbs, uint16_t* __restrict__ dq, int num_tiles,
+               int max_sel, int n_items, int n_padded, float c, float scale) {
+  using C = Cfg<T, D>;
+  constexpr int NDB = C::kDBlocks;
+  __shared__ __attribute__((aligned(1024))) uint16_t ks[T * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t vs[T * D];
+  __shared__ int2 tl[C::kThreads];
+  __shared__ int wave_count[C::kWaves];
+
+  const int item = item_of(blockIdx.x, n_padded);
+  if (item >= n_items) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31;
+  const int half = lane >> 5;
+  const int qrow = wave * 32 + col;
+  const int64_t bh = item / num_tiles;
+  const int tile_i = item - static_cast<int>(bh) * num_tiles;
+  const int64_t head_elems = static_cast<int64_t>(num_tiles) * T * D;
+  const uint16_t* kh = k + bh * head_elems;
+  const uint16_t* vh = v + bh * head_elems;
+  const int64_t row_g = (bh * num_tiles + tile_i) * T + qrow;  // this lane's query row
+  const int vq = clampi(vbs[tile_i], 0, T);
+  const int count = max_sel > 0 ? clampi(q2k_num[item], 0, max_sel) : 0;
+  const int32_t* list = q2k_idx + static_cast<int64_t>(item) * max_sel;
+
+  bf16x8_t qop[C::kKSteps], dop[C::kKSteps];
+#pragma unroll
+  for (int kk = 0; kk < C::kKSteps; ++kk) {
+    qop[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(q + row_g * D + 16 * kk + 8 * half));
+    dop[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(dout + row_g * D + 16 * kk + 8 * half));
+  }
+  const float lse2 = lse[row_g] * kLog2e;
+  const float dlt = delta[row_g];
+
+  f32x16_t acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+  bool any_keys = false;
+  const DmaLane<T, D, false> dl(wave, lane);
+  const f32x16_t zero16 = {};
+
+  for (int base = 0; base < count; base += C::kThreads) {
+    const int total = compact_list<T, C::kWaves>(list, base, count, vbs, num_tiles, tl, wave_count,
+                                                 tid, wave, lane);
+    if (total > 0) any_keys = true;
+    for (int t = 0; t < total; ++t) {
+      const int2 e = tl[t];
+      const int j = __builtin_amdgcn_readfirstlane(e.x);
+      const int vk = __builtin_amdgcn_readfirstlane(e.y);
+      wait_vmcnt<0>();  // the operands loaded above
+      dma_tile<T, D, false>(kh + static_cast<int64_t>(j) * T * D, ks, wave, dl);
+      dma_tile<T, D, false>(vh + static_cast<int64_t>(j) * T * D, vs, wave, dl);
+      wait_vmcnt<0>();
+      if (vk < T) {
+        zero_padding_rows<T, D>(ks, vk, wave, lane);
+        zero_padding_rows<T, D>(vs, vk, wave, lane);
+      }
+      lds_barrier();
+#pragma unroll
+      for (int hh = 0; hh < T / 64; ++hh) {  // 64 keys: key blocks 2*hh, 2*hh + 1
+        f32x16_t s[2], dp[2];
+#pragma unroll
+        for (int kk = 0; kk < C::kKSteps; ++kk)
+#pragma unroll
+          for (int b2 = 0; b2 < 2; ++b2) {
+            s[b2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                read_rows<D>(ks, 32 * (2 * hh + b2), kk, col, half), qop[kk], kk ? s[b2] : zero16, 0, 0, 0);
+            dp[b2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                read_rows<D>(vs, 32 * (2 * hh + b2), kk, col, half), dop[kk], kk ? dp[b2] : zero16, 0, 0, 0);
+          }
+        // P^T = exp2(S^T c - lse2) with keys at or past vk masked; dS^T = P^T (dP^T - D)
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2) {
+          const int kb = 2 * hh + b2;
+          const int t0 = vk - 32 * kb - 4 * half;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const bool masked = 8 * (r >> 2) + (r & 3) >= t0;
+            const float p = masked ? 0.0f : __builtin_amdgcn_exp2f(__builtin_fmaf(s[b2][r], c, -lse2));
+            s[b2][r] = masked ? 0.0f : p * (dp[b2][r] - dlt);
+          }
+        }
+        // dQ^T += K^T dS^T over the four 16-key chunks of this half
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          const bf16x8_t dsk = pack8(s[cc >> 1], 8 * (cc & 1));
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                read_rows_t<D>(ks, 4 * hh + cc, db, lane), dsk, acc[db], 0, 0, 0);
+        }
+      }
+      lds_barrier();  // every wave is done with K and V before the next copies
+    }
+  }
+  wait_vmcnt<0>();
+  const bool zero_row = !any_keys || qrow >= vq;
+  store_t<D>(dq + row_g * D, acc, scale, zero_row, half);
+}
+
+// ---- dK, dV -------------------------------------------------------------------------------
+// At D = 128 a wave holds its K and V operands (64 registers) and two fp32
+// accumulators (128) across the whole list: one wave per SIMD, up to 512
+// registers, instead of spilling at two.
+template <int T, int D>
+__global__ __launch_bounds__(2 * T)
+__attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : 2, D == 128 ? 1 : (T == 128 ? 2 : 4))))
+void dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+                const float* __restrict__ lse, const float* __restrict__ delta,
+                const int32_t* __restrict__ k2q_idx, const int32_t* __restrict__ k2q_num,
+                const int32_t* __restrict__ vbs, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
+                int num_tiles, int max_k, int n_items, int n_padded, float c, float scale) {
+  using C = Cfg<T, D>;
+  constexpr int NDB = C::kDBlocks;
+  __shared__ __attribute__((aligned(1024))) uint16_t qs[T * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t ds_[T * D];  // dO tile
+  __shared__ __attribute__((aligned(16))) float lse_s[T];
+  __shared__ __attribute__((aligned(16))) float dlt_s[T];
+
+  const int item = item_of(blockIdx.x, n_padded);  // (b*H + h) * NT + key tile j
+  if (item >= n_items) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31;
+  const int half = lane >> 5;
+  const int krow = wave * 32 + col;
+  const int64_t bh = item / num_tiles;
+  const int tile_j = item - static_cast<int>(bh) * num_tiles;
+  const int64_t head_elems = static_cast<int64_t>(num_tiles) * T * D;
+  const uint16_t* qh = q + bh * head_elems;
+  const uint16_t* oh = dout + bh * head_elems;
+  const int64_t row_g = (bh * num_tiles + tile_j) * T + krow;  // this lane's key row
+  const int vk = clampi(vbs[tile_j], 0, T);
+  const int count = max_k > 0 ? clampi(k2q_num[item], 0, max_k) : 0;
+  const int32_t* list = k2q_idx + static_cast<int64_t>(item) * max_k;
+
+  bf16x8_t kop[C::kKSteps], vop[C::kKSteps];
+#pragma unroll
+  for (int kk = 0; kk < C::kKSteps; ++kk) {
+    kop[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(k + row_g * D + 16 * kk + 8 * half));
+    vop[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(v + row_g * D + 16 * kk + 8 * half));
+  }
+  f32x16_t acck[NDB], accv[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      acck[db][r] = 0.0f;
+      accv[db][r] = 0.0f;
+    }
+  const DmaLane<T, D, false> dl(wave, lane);
+  const f32x16_t zero16 = {};
+
+  for (int n = 0; n < count; ++n) {
+    const int i = __builtin_amdgcn_readfirstlane(scalar_load(list + n));
+    if (i < 0 || i >= num_tiles) continue;  // uniform
+    const int vq = clampi(scalar_load(vbs + i), 0, T);
+    if (vq == 0) continue;  // uniform
+    const int64_t qtile = static_cast<int64_t>(i) * T;
+    wait_vmcnt<0>();  // the register operands loaded above
+    lds_barrier();    // every wave is done with the previous tiles
+    dma_tile<T, D, false>(qh + qtile * D, qs, wave, dl);
+    dma_tile<T, D, false>(oh + qtile * D, ds_, wave, dl);
+    // staged statistics: padding query rows get lse = +inf, so P = 0 there
+    if (tid < T) {
+      const int64_t r = (bh * num_tiles + i) * T + tid;
+      lse_s[tid] = tid < vq ? lse[r] * kLog2e : INFINITY;
+      dlt_s[tid] = tid < vq ? delta[r] : 0.0f;
+    }
+    wait_vmcnt<0>();
+    if (vq < T) {
+      zero_padding_rows<T, D>(qs, vq, wave, lane);
+      zero_padding_rows<T, D>(ds_, vq, wave, lane);
+    }
+    lds_barrier();
+#pragma unroll
+    for (int qb = 0; qb < T / 32; ++qb) {
+      f32x16_t s = zero16, dp = zero16;
+      // (operand reads stay next to their MFMAs: the register budget holds K, V
+      // and both accumulators, and no more than one step of operands)
+#pragma unroll
+      for (int kk = 0; kk < C::kKSteps; ++kk) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows<D>(qs, 32 * qb, kk, col, half), kop[kk],
+                                                    kk ? s : zero16, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows<D>(ds_, 32 * qb, kk, col, half), vop[kk],
+                                                     kk ? dp : zero16, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // register r holds query 32*qb + 8*(r/4) + 4*half + r%4: statistics four at a time
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 l4 = *reinterpret_cast<const float4*>(lse_s + 32 * qb + 8 * g + 4 * half);
+        const float4 d4 = *reinterpret_cast<const float4*>(dlt_s + 32 * qb + 8 * g + 4 * half);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lv[e]));
+          s[r] = p;                      // P
+          dp[r] = p * (dp[r] - dv4[e]);  // dS
+        }
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS over the two 16-query chunks of this block
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const bf16x8_t pb = pack8(s, 8 * cc);
+        const bf16x8_t sb = pack8(dp, 8 * cc);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          accv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows_t<D>(ds_, 2 * qb + cc, db, lane),
+                                                             pb, accv[db], 0, 0, 0);
+          acck[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows_t<D>(qs, 2 * qb + cc, db, lane),
+                                                             sb, acck[db], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+  }
+  wait_vmcnt<0>();
+  const bool zero_row = krow >= vk;
+  store_t<D>(dk + row_g * D, acck, scale, zero_row, half);
+  store_t<D>(dv + row_g * D, accv, 1.0f, zero_row, half);
+}
+
+template <int T, int D>
+hipError_t launch_grads(const bsa::BwdProblem& p, hipStream_t stream) {
+  const int64_t items = p.batch_heads * p.num_tiles;
+  const int n_items = static_cast<int>(items);
+  const int n_padded = (n_items + 7) / 8 * 8;
+  const float scale = static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(D)));
+  const float c = scale * kLog2e;
+  dim3 block(Cfg<T, D>::kThreads);
+  hipLaunchKernelGGL((dq_kernel<T, D>), dim3(n_padded), block, 0, stream, p.q, p.k, p.v, p.dout,
+                     p.lse, p.delta, p.q2k_idx, p.q2k_num, p.block_sizes, p.dq, p.num_tiles,
+                     p.max_sel, n_items, n_padded, c, scale);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((dkv_kernel<T, D>), dim3(n_padded), block, 0, stream, p.q, p.k, p.v, p.dout,
+                     p.lse, p.delta, p.k2q_idx, p.k2q_num, p.block_sizes, p.dk, p.dv, p.num_tiles,
+                     p.max_k, n_items, n_padded, c, scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+namespace bsa {
+
+hipError_t launch_k2q(const K2qProblem& p, hipStream_t stream) {
+  const int64_t lists = p.batch_heads * p.num_tiles;
+  const int64_t blocks = (lists + 3) / 4;
+  hipLaunchKernelGGL(k2q_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                     p.q2k_idx, p.q2k_num, p.num_tiles, p.max_sel, lists, p.k2q_idx, p.k2q_num,
+                     p.max_k);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
+  const int64_t rows = p.batch_heads * p.num_tiles * p.tile;
+  const int lanes = p.head_dim / 8;
+  const int64_t blocks = (rows * lanes + 255) / 256;
+  if (p.head_dim == 128)
+    hipLaunchKernelGGL(delta_kernel<128>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                       p.out, p.dout, p.block_sizes, p.num_tiles, p.tile, rows, p.delta);
+  else
+    hipLaunchKernelGGL(delta_kernel<64>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                       p.out, p.dout, p.block_sizes, p.num_tiles, p.tile, rows, p.delta);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (p.tile == 128) return p.head_dim == 128 ? launch_grads<128, 128>(p, stream)
+                                               : launch_grads<128, 64>(p, stream);
+  return p.head_dim == 128 ? launch_grads<64, 128>(p, stream) : launch_grads<64, 64>(p, stream);
+}
+
+}  // namespace bsa

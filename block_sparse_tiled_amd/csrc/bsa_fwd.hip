@@ -103,7 +103,7 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     const int32_t* __restrict__ q2k_num, const int32_t* __restrict__ vbs,
                     uint16_t* __restrict__ out, int num_tiles, int max_sel, int n_whole,
                     int n_whole_padded, int n_split_units, int splits, float* __restrict__ ws,
-                    int* __restrict__ counters, float c) {
+                    int* __restrict__ counters, float c, float* __restrict__ lse) {
   using C = Cfg<T, D>;
   using S = Slot<T, D>;
   __shared__ __attribute__((aligned(1024))) uint16_t ks[T * D];
@@ -370,6 +370,14 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
     const bool zero_row = !any_keys || row >= vq;
     const float inv = l_tot != 0.0f ? 1.0f / l_tot : __builtin_nanf("");
+    if (lse != nullptr && ln < 32) {
+      // natural-log log-sum-exp of the scaled logits: (m*c + log2 l) * ln 2,
+      // with the exponent offset m*c taken as 0 while m is -inf (then l is 0
+      // and the result -inf); -inf for padding rows and rows without keys
+      const float mc = (m_run == -INFINITY ? 0.0f : m_run) * c;
+      lse[(ibh * num_tiles + itile) * T + row] =
+          zero_row ? -INFINITY : (mc + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+    }
     uint16_t* dst = out + ((ibh * num_tiles + itile) * T + row) * D + 4 * (ln >> 5);
 #pragma unroll
     for (int db = 0; db < C::kDBlocks; ++db)
@@ -482,6 +490,7 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
       }
   }
   any_keys = any_all;
+  m_run = mm;
   store_rows();
 }
 
@@ -503,8 +512,9 @@ hipError_t launch(const bsa::FwdProblem& p, hipStream_t stream) {
   float* ws = p.ws;
   int* counters = p.counters;
   float cc = c;
+  float* lse = p.lse;
   void* args[] = {&q, &k, &v, &idx, &num, &vbs, &out, &nt, &ms, &n_whole, &n_whole_padded,
-                  &n_split_units, &splits, &ws, &counters, &cc};
+                  &n_split_units, &splits, &ws, &counters, &cc, &lse};
   const int units = n_whole_padded + n_split_units;
   return hipLaunchKernel(fn, dim3(static_cast<unsigned>(units)), block, args, 0, stream);
 }

@@ -28,6 +28,7 @@ struct FwdProblem {
   int32_t splits;
   float* ws;              // n_split_units partial slots (when splits > 1)
   int32_t* counters;      // one arrival counter per split item, zero between launches
+  float* lse;             // [B, H, NT*T] log-sum-exp per row, or null
 };
 
 // How the items are cut into work units, and the workspace that needs (none
@@ -56,6 +57,47 @@ struct LayoutProblem {
 };
 
 hipError_t launch_tile_layout(const LayoutProblem& p, hipStream_t stream);
+
+// Transposed lists for the backward: for each key tile, the query tiles whose
+// lists name it (ascending; a tile listed twice appears twice).
+struct K2qProblem {
+  const int32_t* q2k_idx;  // may be null when max_sel == 0
+  const int32_t* q2k_num;
+  int32_t* k2q_idx;        // [B, H, NT, max_k]
+  int32_t* k2q_num;        // [B, H, NT], the true counts
+  int64_t batch_heads;
+  int32_t num_tiles;
+  int32_t max_sel;
+  int32_t max_k;
+};
+
+hipError_t launch_k2q(const K2qProblem& p, hipStream_t stream);
+
+struct BwdProblem {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* out;
+  const uint16_t* dout;
+  const float* lse;
+  const int32_t* q2k_idx;
+  const int32_t* q2k_num;
+  const int32_t* k2q_idx;
+  const int32_t* k2q_num;
+  const int32_t* block_sizes;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* delta;  // [B, H, NT*T] workspace
+  int64_t batch_heads;
+  int32_t num_tiles;
+  int32_t max_sel;
+  int32_t max_k;
+  int32_t tile;
+  int32_t head_dim;
+};
+
+hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream);
 
 // The inverse gather: p.src are tile buffers, p.dst token-major outputs, and
 // p.tile_src_token holds the tile row of every token (token_row).

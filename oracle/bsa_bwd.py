@@ -19,7 +19,8 @@ valid key rows in list order, a tile listed twice counted twice):
 Rows without keys and padding query rows (r >= block_sizes[i]) have a
 constant output (+0), so they produce no gradient; padding key rows are never
 read, so their dk and dv are 0.  lse_r = log sum exp(s) in natural-log units,
--inf for rows without keys and for padding rows.
+-inf for rows without keys, for padding rows and for rows whose logits are all
+-inf (log 0; their output is the NaN row of the hardening commit).
 """
 from __future__ import annotations
 
@@ -90,7 +91,9 @@ def fwd64(q, k, v, q2k_idx, q2k_num, vbs, tile):
                     p = np.exp(s - m)
                     l = p.sum(axis=1, keepdims=True)
                     out[b, h, rows] = (p / l) @ v[b, h, keys]
-                    lse[b, h, rows] = (m + np.log(l))[:, 0]
+                    # log sum exp(s): log 0 = -inf when every logit is -inf (the max
+                    # shift would give -inf - -inf there)
+                    lse[b, h, rows] = np.where(np.isneginf(m), -np.inf, m + np.log(l))[:, 0]
     return out, lse
 
 

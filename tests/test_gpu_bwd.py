@@ -1,0 +1,189 @@
+"""GPU parity of the log-sum-exp forward and the backward (bsa_fwd_lse, bsa_bwd_k2q,
+bsa_bwd) against the fp64 oracle (oracle.bsa_bwd), through the C ABI.
+
+Compare rule for gradients (bf16 on the GPU, fp64 in the oracle): NaN
+positions identical; rows the oracle leaves at exactly 0 (padding rows, rows in
+no listed pair) are +0 bit for bit; over the other elements, with s =
+max(1, RMS of the oracle's finite values), max |diff| <= 2e-2 s and mean |diff|
+<= 2e-3 s: the forward's bar, on the gradients' own scale.  (Measured on the
+random and config shapes: max about 5e-3, mean about 2e-4.)  The transposed
+lists are compared bit for bit.
+"""
+import numpy as np
+import pytest
+
+import block_sparse_tiled_amd as bsa
+from block_sparse_tiled_amd import inputs as gen
+from parity import bits_from_dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+MAX_REL = 2e-2
+MEAN_REL = 2e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    bsa.load()
+
+
+def k2q_reference(q2k_idx, q2k_num, NT):
+    B, H = q2k_num.shape[:2]
+    lists = [[[[] for _ in range(NT)] for _ in range(H)] for _ in range(B)]
+    for b in range(B):
+        for h in range(H):
+            for i in range(NT):
+                for j in q2k_idx[b, h, i, :q2k_num[b, h, i]]:
+                    if 0 <= j < NT:
+                        lists[b][h][j].append(i)
+    return lists
+
+
+def run_all(w, dout_bits, max_k=None):
+    import torch
+
+    q, k, v = (to_dev(x) for x in (w.q, w.k, w.v))
+    idx, num, vbs = to_dev(w.q2k_idx), to_dev(w.q2k_num), to_dev(w.vbs)
+    out, lse = bsa.fwd_lse(q, k, v, idx, num, vbs, w.T)
+    k2q_idx, k2q_num = bsa.bwd_k2q(idx, num, max_k=max_k)
+    dq, dk, dv = bsa.bwd(q, k, v, out, to_dev(dout_bits), lse, idx, num, k2q_idx, k2q_num, vbs,
+                         w.T)
+    torch.cuda.synchronize()
+    return {"out": bits_from_dev(out), "lse": lse.cpu().numpy(), "dq": bits_from_dev(dq),
+            "dk": bits_from_dev(dk), "dv": bits_from_dev(dv),
+            "k2q_idx": k2q_idx.cpu().numpy(), "k2q_num": k2q_num.cpu().numpy()}
+
+
+def compare_grad(got_bits, ref, label):
+    got = gen.bf16_bits_to_f32(got_bits).astype(np.float64)
+    nan_ref, nan_got = np.isnan(ref), np.isnan(got)
+    assert np.array_equal(nan_ref, nan_got), (
+        f"{label}: NaN mask differs ({int(nan_ref.sum())} oracle, {int(nan_got.sum())} GPU)")
+    zero_rows = np.all(ref == 0, axis=-1)
+    assert np.all(got_bits[zero_rows] == 0), f"{label}: rows the oracle leaves at 0 are not +0"
+    fin = np.isfinite(ref) & ~nan_ref
+    assert np.array_equal(np.isinf(got), np.isinf(ref)), f"{label}: Inf mask differs"
+    diff = np.abs(got[fin] - ref[fin])
+    s = max(1.0, float(np.sqrt(np.mean(ref[fin] ** 2)))) if fin.any() else 1.0
+    mx = float(diff.max()) if diff.size else 0.0
+    mean = float(diff.mean()) if diff.size else 0.0
+    print(f"{label}: max {mx:.3e} mean {mean:.3e} (scale {s:.3f})", flush=True)
+    assert mx <= MAX_REL * s and mean <= MEAN_REL * s, f"{label}: max {mx:.3e} mean {mean:.3e} scale {s:.3f}"
+    return mx / s, mean / s
+
+
+def check_problem(w, seed, label, max_k=None):
+    rng = np.random.default_rng(seed)
+    dout = gen.to_bf16_bits(rng.standard_normal(w.q.shape).astype(np.float32))
+    got = run_all(w, dout, max_k=max_k)
+    # forward output unchanged by the LSE variant
+    np.testing.assert_array_equal(got["out"], bits_from_dev(bsa.fwd(
+        to_dev(w.q), to_dev(w.k), to_dev(w.v), to_dev(w.q2k_idx), to_dev(w.q2k_num),
+        to_dev(w.vbs), w.T)))
+    import oracle
+
+    out64, lse64 = oracle.fwd64(w.q, w.k, w.v, w.q2k_idx, w.q2k_num, w.vbs, w.T)
+    assert np.array_equal(np.isneginf(got["lse"]), np.isneginf(lse64)), f"{label}: lse -inf mask"
+    assert np.array_equal(np.isnan(got["lse"]), np.isnan(lse64)), f"{label}: lse NaN mask"
+    fin = np.isfinite(lse64)
+    np.testing.assert_allclose(got["lse"][fin], lse64[fin], rtol=1e-5, atol=1e-4)
+    # transposed lists: order and counts exactly
+    NT = w.NT
+    ref_lists = k2q_reference(w.q2k_idx, w.q2k_num, NT)
+    for b in range(w.B):
+        for h in range(w.H):
+            for j in range(NT):
+                lst = ref_lists[b][h][j]
+                assert got["k2q_num"][b, h, j] == len(lst)
+                n = min(len(lst), got["k2q_idx"].shape[3])
+                assert got["k2q_idx"][b, h, j, :n].tolist() == lst[:n]
+    dq, dk, dv = oracle.bwd(w.q, w.k, w.v, dout, w.q2k_idx, w.q2k_num, w.vbs, w.T)
+    compare_grad(got["dq"], dq, f"{label} dq")
+    compare_grad(got["dk"], dk, f"{label} dk")
+    compare_grad(got["dv"], dv, f"{label} dv")
+
+
+@pytest.mark.parametrize("T,D", [(64, 64), (64, 128), (128, 64), (128, 128)])
+def test_random_ragged_lists(T, D):
+    w = gen.random_problem(60 + T + D, B=1, H=2, D=D, T=T, vbs=[T, T - 5, 1, T, T // 2 + 3, T],
+                           density=0.5, pad="nan")
+    print(f"bwd random T={T} D={D}", flush=True)
+    check_problem(w, 1, f"random T={T} D={D}")
+
+
+def test_duplicates_and_empty_tiles():
+    T, D = 128, 128
+    w = gen.random_problem(70, B=2, H=1, D=D, T=T, vbs=[T, 0, 77, T], counts=3, MS=3,
+                           duplicates=True, pad="inf")
+    w.q2k_num[0, 0, 2] = 0
+    print("bwd duplicates", flush=True)
+    check_problem(w, 2, "duplicates", max_k=3 * w.NT)
+
+
+def test_tiny_config():
+    w = gen.tiny()
+    print("bwd tiny", flush=True)
+    check_problem(w, 3, "tiny")
+
+
+def test_ragged_config_every_row():
+    w = gen.ragged()
+    print("bwd ragged", flush=True)
+    check_problem(w, 4, "ragged")
+
+
+def test_deterministic():
+    import torch
+
+    w = gen.random_problem(80, B=1, H=2, D=128, T=128, vbs=[128] * 6, density=0.7)
+    rng = np.random.default_rng(5)
+    dout = gen.to_bf16_bits(rng.standard_normal(w.q.shape).astype(np.float32))
+    a = run_all(w, dout)
+    b = run_all(w, dout)
+    for key in ("dq", "dk", "dv", "k2q_idx", "k2q_num"):
+        np.testing.assert_array_equal(a[key], b[key])
+    torch.cuda.synchronize()
+
+
+def test_nan_row_and_inf_padding():
+    """The stress construction in small: K/V padding rows hold NaN and +-Inf, and one
+    query row has only -inf logits (a NaN row, hardening commit); its gradient is NaN in
+    dq and in the dk/dv rows of every key it lists, as in the plain formula."""
+    T, D = 128, 128
+    w = gen.random_problem(90, B=1, H=2, D=D, T=T, vbs=[T, 100, 37, T], density=0.6,
+                           pad="naninf")
+    b, h, i = 0, 1, 0
+    w.q2k_num[b, h, i] = max(int(w.q2k_num[b, h, i]), 1)
+    r = i * T + 5
+    qf = gen.bf16_bits_to_f32(w.q)
+    kf = gen.bf16_bits_to_f32(w.k)
+    qf[b, h, r] = 0.0
+    qf[b, h, r, 0] = -np.inf
+    for t in range(w.NT):
+        rows = slice(t * T, t * T + int(w.vbs[t]))
+        kf[b, h, rows, 0] = np.abs(kf[b, h, rows, 0]) + 1
+    w.q[...] = gen.to_bf16_bits(qf)
+    w.k[...] = gen.to_bf16_bits(kf)
+    print("bwd nan row", flush=True)
+    check_problem(w, 6, "nan row")
+
+
+def test_rising_logits():
+    """Key tiles scaled up along the list, so that the forward's lazy exponent offset
+    moves several times within a list (raw maxima rise by more than its slack); the
+    log-sum-exp and the gradients follow.  (Much larger logits make rows so peaked that
+    dS is a small difference of two nearly equal terms, and the bf16 rounding of the
+    stored output, through D = dO . out, dominates the gradient error; the bar here is
+    for softmax of ordinary sharpness.)"""
+    T, D, NT = 128, 128, 6
+    w = gen.random_problem(91, B=1, H=2, D=D, T=T, vbs=[T] * (NT - 1) + [T - 9], counts=NT, MS=NT)
+    w.q[...] = gen.to_bf16_bits(gen.bf16_bits_to_f32(w.q) * 1.5)
+    for j in range(NT):
+        sl = slice(j * T, (j + 1) * T)
+        w.k[:, :, sl] = gen.to_bf16_bits(gen.bf16_bits_to_f32(w.k[:, :, sl]) * (0.25 + 0.25 * j))
+    print("bwd rising logits", flush=True)
+    check_problem(w, 7, "rising logits")

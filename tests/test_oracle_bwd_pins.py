@@ -171,5 +171,6 @@ def test_all_minus_inf_row_has_nan_gradients():
     out, lse = oracle.fwd64(q, k, w.v, w.q2k_idx, w.q2k_num, w.vbs, T)
     dq, dk, dv = oracle.bwd(q, k, w.v, dout, w.q2k_idx, w.q2k_num, w.vbs, T)
     assert np.all(np.isnan(out[0, 0, 5])) and np.all(np.isnan(dq[0, 0, 5]))
+    assert np.isneginf(lse[0, 0, 5])  # log of a sum of zeros
     others = np.setdiff1d(np.arange(2 * T), [5])
     assert np.isfinite(out[0, 0, others]).all() and np.isfinite(dq[0, 0, others]).all()
