@@ -120,6 +120,79 @@ def cpu_baseline(w, kv, budget_flops):
     }
 
 
+def run_backward(args, w, flops_fwd, put, dev):
+    """One training pass of the attention: bsa_fwd_lse, bsa_bwd_k2q and bsa_bwd, inputs
+    resident in HBM.  Algorithmic backward FLOPs: the five products of the plain
+    backward (S recomputed, dP, dV, dQ, dK), 2.5 times the forward's valid-token count."""
+    import torch
+
+    import block_sparse_tiled_amd as bsa
+
+    q, k, v = put(w.q), put(w.k), put(w.v)
+    idx, num, vbs = put(w.q2k_idx), put(w.q2k_num), put(w.vbs)
+    rng = np.random.default_rng(17)
+    from block_sparse_tiled_amd import inputs as gen
+
+    dout = put(gen.to_bf16_bits(rng.standard_normal(w.q.shape).astype(np.float32)))
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        bsa.fwd_lse(q, k, v, idx, num, vbs, w.T, out=out, lse=lse)
+        if ev is not None:
+            ev[1].record(stream)
+        k2q_idx, k2q_num = bsa.bwd_k2q(idx, num)
+        if ev is not None:
+            ev[2].record(stream)
+        bsa.bwd(q, k, v, out, dout, lse, idx, num, k2q_idx, k2q_num, vbs, w.T, dq=dq, dk=dk, dv=dv)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for st in range(args.steps):
+        step(events[st])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = lambda a, b: float(np.mean([e[a].elapsed_time(e[b]) for e in events]))  # noqa: E731
+    fwd_ms, k2q_ms, bwd_ms = ms(0, 1), ms(1, 2), ms(2, 3)
+    flops_bwd = int(2.5 * flops_fwd)
+    ms_step = wall * 1e3 / args.steps
+    rec = {
+        "metric": "backward effective TFLOPS (selected tiles only) + % bf16 MFMA peak, ms/call",
+        "value": round(flops_bwd / (bwd_ms * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[args.workload], "B": w.B, "H": w.H, "D": w.D,
+                   "tile": w.T, "num_tiles": w.NT, "max_sel": w.MS,
+                   "flops_bwd_valid_tokens": flops_bwd,
+                   "step": "bsa_fwd_lse + bsa_bwd_k2q + bsa_bwd (delta, dQ, dK/dV kernels)"},
+        "fwd_lse_ms": round(fwd_ms, 5),
+        "k2q_ms": round(k2q_ms, 5),
+        "bwd_ms": round(bwd_ms, 5),
+        "train_pass_tflops": round((flops_fwd + flops_bwd) / (ms_step * 1e-3) / 1e12, 3),
+        "roofline": {"bound": "mfma", "kernel": "bsa_bwd (delta + dq_kernel + dkv_kernel)",
+                     "achieved": round(flops_bwd / (bwd_ms * 1e-3) / 1e12, 3),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flops_bwd / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -131,6 +204,9 @@ def main():
                     help="size of the row sample the CPU oracle is timed on")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB copy kernel (HBM counter calibration)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the training pass instead: log-sum-exp forward, transposed lists, "
+                         "backward (prints its own JSON line)")
     ap.add_argument("--fwd-only", action="store_true",
                     help="time only the attention launch (no layout) -- for profiling")
     args = ap.parse_args()
@@ -160,6 +236,10 @@ def main():
         if a.dtype == np.uint16:
             return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(a).to(dev)
+
+    if args.backward:
+        run_backward(args, w, flops, put, dev)
+        return
 
     tok = [put(w.tok[x]) for x in ("q", "k", "v", "gate")]
     src_map = put(w.tile_src_token)
