@@ -301,10 +301,14 @@ void dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 int num_tiles, int max_k, int n_items, int n_padded, float c, float scale) {
   using C = Cfg<T, D>;
   constexpr int NDB = C::kDBlocks;
-  __shared__ __attribute__((aligned(1024))) uint16_t qs[T * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t ds_[T * D];  // dO tile
-  __shared__ __attribute__((aligned(16))) float lse_s[T];
-  __shared__ __attribute__((aligned(16))) float dlt_s[T];
+  // Q and dO tiles and their row statistics, double-buffered: the copies of
+  // the next query tile land while the current one is computed.
+  __shared__ __attribute__((aligned(1024))) uint16_t qs_all[2][T * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t ds_all[2][T * D];  // dO tiles
+  __shared__ __attribute__((aligned(16))) float lse_all[2][T];
+  __shared__ __attribute__((aligned(16))) float dlt_all[2][T];
+  __shared__ int2 tl[C::kThreads];  // usable entries of the current list chunk: (tile, length)
+  __shared__ int wave_count[C::kWaves];
 
   const int item = item_of(blockIdx.x, n_padded);  // (b*H + h) * NT + key tile j
   if (item >= n_items) return;
@@ -341,33 +345,52 @@ void dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const DmaLane<T, D, false> dl(wave, lane);
   const f32x16_t zero16 = {};
 
-  for (int n = 0; n < count; ++n) {
-    const int i = __builtin_amdgcn_readfirstlane(scalar_load(list + n));
-    if (i < 0 || i >= num_tiles) continue;  // uniform
-    const int vq = clampi(scalar_load(vbs + i), 0, T);
-    if (vq == 0) continue;  // uniform
+  // Copies of usable entry t of the chunk (query tile i, vq valid rows) into
+  // buffer `buf`; its statistics go to registers (threads below T), written
+  // to LDS once they have landed.
+  float l_next = 0.0f, d_next = 0.0f;
+  auto issue = [&](int t, int buf) {
+    const int2 e = tl[t];
+    const int i = __builtin_amdgcn_readfirstlane(e.x);
+    const int vq = __builtin_amdgcn_readfirstlane(e.y);
     const int64_t qtile = static_cast<int64_t>(i) * T;
-    wait_vmcnt<0>();  // the register operands loaded above
-    lds_barrier();    // every wave is done with the previous tiles
-    dma_tile<T, D, false>(qh + qtile * D, qs, wave, dl);
-    dma_tile<T, D, false>(oh + qtile * D, ds_, wave, dl);
-    // staged statistics: padding query rows get lse = +inf, so P = 0 there
-    if (tid < T) {
+    dma_tile<T, D, false>(qh + qtile * D, qs_all[buf], wave, dl);
+    dma_tile<T, D, false>(oh + qtile * D, ds_all[buf], wave, dl);
+    if (tid < vq) {
       const int64_t r = (bh * num_tiles + i) * T + tid;
-      lse_s[tid] = tid < vq ? lse[r] * kLog2e : INFINITY;
-      dlt_s[tid] = tid < vq ? delta[r] : 0.0f;
+      l_next = lse[r];
+      d_next = delta[r];
     }
-    wait_vmcnt<0>();
-    if (vq < T) {
-      zero_padding_rows<T, D>(qs, vq, wave, lane);
-      zero_padding_rows<T, D>(ds_, vq, wave, lane);
-    }
-    lds_barrier();
+  };
+
+  for (int base = 0; base < count; base += C::kThreads) {
+    const int total = compact_list<T, C::kWaves>(list, base, count, vbs, num_tiles, tl, wave_count,
+                                                 tid, wave, lane);
+    if (total == 0) continue;
+    wait_vmcnt<0>();  // the register operands loaded above
+    issue(0, 0);
+    for (int t = 0; t < total; ++t) {
+      const int buf = t & 1;
+      const int vq = __builtin_amdgcn_readfirstlane(tl[t].y);
+      uint16_t* qs = qs_all[buf];
+      uint16_t* ds_ = ds_all[buf];
+      float* lse_s = lse_all[buf];
+      float* dlt_s = dlt_all[buf];
+      wait_vmcnt<0>();  // tile t's copies and statistics have landed
+      // padding query rows get lse = +inf, so P = 0 there
+      if (tid < T) {
+        lse_s[tid] = tid < vq ? l_next * kLog2e : INFINITY;
+        dlt_s[tid] = tid < vq ? d_next : 0.0f;
+      }
+      if (vq < T) {
+        zero_padding_rows<T, D>(qs, vq, wave, lane);
+        zero_padding_rows<T, D>(ds_, vq, wave, lane);
+      }
+      lds_barrier();  // tile t visible; every wave is done with tile t - 1's buffer
+      if (t + 1 < total) issue(t + 1, buf ^ 1);
 #pragma unroll
     for (int qb = 0; qb < T / 32; ++qb) {
       f32x16_t s = zero16, dp = zero16;
-      // (operand reads stay next to their MFMAs: the register budget holds K, V
-      // and both accumulators, and no more than one step of operands)
 #pragma unroll
       for (int kk = 0; kk < C::kKSteps; ++kk) {
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows<D>(qs, 32 * qb, kk, col, half), kop[kk],
@@ -405,6 +428,7 @@ void dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         }
       }
     }
+  }
   }
   wait_vmcnt<0>();
   const bool zero_row = krow >= vk;
