@@ -45,33 +45,67 @@ namespace {
 using namespace bsa::detail;
 
 // ---- transposed lists ---------------------------------------------------------------------
+// One wave per (head, key tile j) scans the head's lists in order (ascending
+// query tile, then list position) and appends i for every live entry equal
+// to j through a ballot-ordered prefix.  Lists of 64 or more positions are
+// read row by row (the count read once per row, 64 contiguous entries per
+// load); shorter ones as one flat range of [NT][MS] entries with four loads
+// in flight, so that a wave does not wait once per short row.
+__device__ __forceinline__ void k2q_append(bool hit, int value, int& count, int32_t* dst, int max_k,
+                                           int lane) {
+  const uint64_t m = __ballot(hit);
+  if (hit) {
+    (void)lane;
+    const int at = count + __builtin_amdgcn_mbcnt_hi(
+                               static_cast<uint32_t>(m >> 32),
+                               __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
+    if (at < max_k) dst[at] = value;
+  }
+  count += __popcll(m);
+}
+
 __global__ __launch_bounds__(256) void k2q_kernel(const int32_t* __restrict__ q2k_idx,
                                                   const int32_t* __restrict__ q2k_num,
                                                   int num_tiles, int max_sel, int64_t n_lists,
                                                   int32_t* __restrict__ k2q_idx,
                                                   int32_t* __restrict__ k2q_num, int max_k) {
+  constexpr int kU = 4;
   const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (wid >= n_lists) return;  // whole waves leave together
   const int64_t bh = wid / num_tiles;
   const int j = static_cast<int>(wid - bh * num_tiles);
-  const int32_t* idx_h = q2k_idx + bh * num_tiles * static_cast<int64_t>(max_sel);
+  const int64_t entries = static_cast<int64_t>(num_tiles) * max_sel;
+  const int32_t* idx_h = q2k_idx + bh * entries;
   const int32_t* num_h = q2k_num + bh * num_tiles;
   int32_t* dst = k2q_idx + wid * max_k;
   int count = 0;
-  for (int i = 0; i < num_tiles; ++i) {
-    const int n = max_sel > 0 ? clampi(num_h[i], 0, max_sel) : 0;
-    for (int base = 0; base < n; base += 64) {
-      const int e = base + lane;
-      const bool hit = e < n && idx_h[static_cast<int64_t>(i) * max_sel + e] == j;
-      const uint64_t m = __ballot(hit);
-      if (hit) {
-        const int pos = count + __builtin_amdgcn_mbcnt_hi(
-                                    static_cast<uint32_t>(m >> 32),
-                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
-        if (pos < max_k) dst[pos] = i;
+  if (max_sel >= 64 || entries + 64 * kU >= (int64_t{1} << 31)) {
+    for (int i = 0; i < num_tiles; ++i) {
+      const int n = clampi(num_h[i], 0, max_sel);
+      for (int base = 0; base < n; base += 64) {
+        const int e = base + lane;
+        k2q_append(e < n && idx_h[static_cast<int64_t>(i) * max_sel + e] == j, i, count, dst, max_k,
+                   lane);
       }
-      count += __popcll(m);
+    }
+  } else {
+    const uint32_t ms = static_cast<uint32_t>(max_sel);  // entries < 2^31 here
+    for (uint32_t base = 0; base < entries; base += 64 * kU) {
+      bool hit[kU];
+      int row[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const uint32_t pos = base + 64 * u + lane;
+        row[u] = static_cast<int>(pos / ms);
+        hit[u] = false;
+        if (pos < entries) {
+          const int e = static_cast<int>(pos - row[u] * ms);
+          hit[u] = e < clampi(num_h[row[u]], 0, max_sel) && idx_h[pos] == j;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) k2q_append(hit[u], row[u], count, dst, max_k, lane);
     }
   }
   if (lane == 0) k2q_num[wid] = count;  // the true count (the list holds the first max_k)
