@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(HERE, "libbsa.so")
 MAX_BATCH_HEADS = 65535
 ROWS_LIMIT = 1 << 31
 TILES_LIMIT = 1 << 22
-TILES = (64, 128)
+TILES = (64, 128, 256)   # forward, layout; the backward takes 64 or 128
+BWD_TILES = (64, 128)
 HEAD_DIMS = (64, 128)
 
 STATUS = {
@@ -153,7 +154,7 @@ def fwd(q, k, v, q2k_idx, q2k_num, block_sizes, tile, out=None):
         raise ValueError("q, k and v must have the same shape")
     B, H, S, D = q.shape
     if tile not in TILES:
-        raise ValueError(f"tile must be 64 or 128, got {tile}")
+        raise ValueError(f"tile must be 64, 128 or 256, got {tile}")
     if S % tile:
         raise ValueError(f"sequence length {S} is not a multiple of the tile {tile}")
     NT = S // tile
@@ -200,7 +201,7 @@ def tile_layout(srcs, tile_src_token, tile, outs=None):
     B, S_tok, H, D = srcs[0].shape
     rows = tile_src_token.shape[0]
     if tile not in TILES or rows % tile:
-        raise ValueError("the map must cover a whole number of 64- or 128-row tiles")
+        raise ValueError("the map must cover a whole number of 64-, 128- or 256-row tiles")
     NT = rows // tile
     if outs is None:
         outs = [torch.empty((B, H, rows, D), dtype=torch.bfloat16, device=device) for _ in srcs]
@@ -243,7 +244,7 @@ def tile_unlayout(tiled, token_row, tile, tokens=None, outs=None):
     _require(token_row, "token_row", torch.int32, device, 1)
     B, H, rows, D = tiled[0].shape
     if tile not in TILES or rows % tile:
-        raise ValueError("the tile buffers must hold a whole number of 64- or 128-row tiles")
+        raise ValueError("the tile buffers must hold a whole number of 64-, 128- or 256-row tiles")
     S_tok = token_row.shape[0] if tokens is None else tokens
     if token_row.shape[0] != S_tok:
         raise ValueError("token_row must have one entry per token")
@@ -302,7 +303,7 @@ def _fwd_args(q, k, v, q2k_idx, q2k_num, block_sizes, tile):
         raise ValueError("q, k and v must have the same shape")
     B, H, S, D = q.shape
     if tile not in TILES:
-        raise ValueError(f"tile must be 64 or 128, got {tile}")
+        raise ValueError(f"tile must be 64, 128 or 256, got {tile}")
     if S % tile:
         raise ValueError(f"sequence length {S} is not a multiple of the tile {tile}")
     NT = S // tile
@@ -363,6 +364,8 @@ def bwd(q, k, v, out, dout, lse, q2k_idx, q2k_num, k2q_idx, k2q_num, block_sizes
     import torch
 
     lib = load()
+    if tile not in BWD_TILES:
+        raise ValueError(f"the backward takes tiles of 64 or 128 rows, got {tile}")
     device, B, H, S, D, NT = _fwd_args(q, k, v, q2k_idx, q2k_num, block_sizes, tile)
     for t, name in ((out, "out"), (dout, "dout")):
         _require(t, name, torch.bfloat16, device, 4)

@@ -103,12 +103,15 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     const int32_t* __restrict__ q2k_num, const int32_t* __restrict__ vbs,
                     uint16_t* __restrict__ out, int num_tiles, int max_sel, int n_whole,
                     int n_whole_padded, int n_split_units, int splits, float* __restrict__ ws,
-                    int* __restrict__ counters, float c, float* __restrict__ lse) {
+                    int* __restrict__ counters, float c, float* __restrict__ lse,
+                    int sub_shift) {
   using C = Cfg<T, D>;
   using S = Slot<T, D>;
   __shared__ __attribute__((aligned(1024))) uint16_t ks[T * D];
   __shared__ __attribute__((aligned(1024))) uint16_t vs[T * D];
-  __shared__ int2 tl[C::kThreads];  // usable list entries of the current chunk: (tile, length)
+  // usable list entries of the current chunk, (tile, length); two per list
+  // entry when the lists name tiles of 2T rows
+  __shared__ int2 tl[(T == 128 ? 2 : 1) * C::kThreads];
   __shared__ int wave_count[C::kWaves];
   __shared__ int arrival;
 
@@ -153,8 +156,14 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   const uint16_t* qh = q + bh * head_elems;
   const uint16_t* kh = k + bh * head_elems;
   const uint16_t* vh = v + bh * head_elems;
-  const int count = max_sel > 0 ? clampi(q2k_num[item], 0, max_sel) : 0;
-  const int32_t* list = q2k_idx + static_cast<int64_t>(item) * max_sel;
+  // Lists and lengths count tiles of T << sub_shift rows ("list tiles"); the
+  // kernel works on T-row tiles, sub_shift + 1 of them per list tile (the
+  // row layout is the same).
+  const int nt_list = num_tiles >> sub_shift;
+  const int tile_l = tile_i >> sub_shift;
+  const int64_t item_l = bh * nt_list + tile_l;
+  const int count = max_sel > 0 ? clampi(q2k_num[item_l], 0, max_sel) : 0;
+  const int32_t* list = q2k_idx + item_l * max_sel;
   const int end = b < count ? b : count;
 
   // Q^T operand (B of the first product): lane (query col, half) holds
@@ -359,7 +368,7 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   auto store_rows = [&]() {
     const int64_t ibh = item / num_tiles;
     const int itile = item - static_cast<int>(ibh) * num_tiles;
-    const int vq = clampi(vbs[itile], 0, T);
+    const int vq = clampi(vbs[itile >> sub_shift] - T * (itile & ((1 << sub_shift) - 1)), 0, T);
     const int ln = launder(lane);  // per-lane addresses computed here, not hoisted
     const int row = wave * 32 + (ln & 31);
     float l_tot;
@@ -398,8 +407,8 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   // The segment in chunks of kThreads list entries; within a chunk the tiles
   // are pipelined (the copies of the next tile overlap the current one).
   for (int base = a; base < end; base += C::kThreads) {
-    const int total = compact_list<T, C::kWaves>(list, base, end, vbs, num_tiles, tl, wave_count, tid,
-                                                 wave, lane);
+    const int total = compact_list<T, C::kWaves>(list, base, end, vbs, nt_list, tl, wave_count, tid,
+                                                 wave, lane, sub_shift);
     if (total == 0) continue;
     any_keys = true;
     int2 e = tl[0];
@@ -513,8 +522,9 @@ hipError_t launch(const bsa::FwdProblem& p, hipStream_t stream) {
   int* counters = p.counters;
   float cc = c;
   float* lse = p.lse;
+  int sub_shift = p.sub_shift;
   void* args[] = {&q, &k, &v, &idx, &num, &vbs, &out, &nt, &ms, &n_whole, &n_whole_padded,
-                  &n_split_units, &splits, &ws, &counters, &cc, &lse};
+                  &n_split_units, &splits, &ws, &counters, &cc, &lse, &sub_shift};
   const int units = n_whole_padded + n_split_units;
   return hipLaunchKernel(fn, dim3(static_cast<unsigned>(units)), block, args, 0, stream);
 }

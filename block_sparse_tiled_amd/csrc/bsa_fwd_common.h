@@ -203,24 +203,28 @@ __device__ __forceinline__ void zero_padding_rows(uint16_t* lds, int vk, int wav
 
 // Copies the usable entries of list[base, min(base + 64*NW, count)) -- in
 // range and with at least one valid key -- into tl[] in list order, with
-// their valid lengths (clamped to T); returns how many there are (uniform).
-// One entry per thread of an NW-wave workgroup; the order is kept by a
-// wave-level prefix count (mbcnt) plus per-wave offsets.  Three barriers.
+// their valid lengths (clamped); returns how many there are (uniform).
+// With sub_shift = 1 the list names tiles of 2T rows (lengths up to 2T), and
+// each entry becomes its non-empty T-row halves (tile 2j + t, t = 0, 1), in
+// order: tl[] then holds up to 2 * 64 * NW entries.  One list entry per thread
+// of an NW-wave workgroup; the order is kept by wave-level prefix counts
+// (mbcnt) plus per-wave offsets.  Three barriers.
 template <int T, int NW>
 __device__ __forceinline__ int compact_list(const int32_t* __restrict__ list, int base, int count,
                                             const int32_t* __restrict__ vbs, int num_tiles,
                                             int2* tl, int* wave_count, int tid, int wave,
-                                            int lane) {
+                                            int lane, int sub_shift = 0) {
   const int e = base + tid;
   int jj = -1, len = 0;
   if (e < count) {
     jj = list[e];
-    if (jj >= 0 && jj < num_tiles) len = clampi(vbs[jj], 0, T);
+    if (jj >= 0 && jj < num_tiles) len = clampi(vbs[jj], 0, T << sub_shift);
   }
-  const bool ok = len > 0;
-  const uint64_t m = __ballot(ok);
+  const int parts = (len + T - 1) / T;  // non-empty T-row parts, a prefix of the tile
+  const uint64_t m1 = __ballot(parts >= 1);
+  const uint64_t m2 = __ballot(parts >= 2);
   lds_barrier();  // the previous chunk's readers of tl[] and wave_count[] are done
-  if (lane == 0) wave_count[wave] = __popcll(m);
+  if (lane == 0) wave_count[wave] = __popcll(m1) + __popcll(m2);
   lds_barrier();
   int off = 0, total = 0;
 #pragma unroll
@@ -229,9 +233,13 @@ __device__ __forceinline__ int compact_list(const int32_t* __restrict__ list, in
     off += w < wave ? cw : 0;
     total += cw;
   }
-  const int pos = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
-                                            __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
-  if (ok) tl[off + pos] = make_int2(jj, len);
+  auto below = [&](uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
+  };
+  const int pos = below(m1) + below(m2);
+  for (int t = 0; t < parts; ++t)
+    tl[off + pos + t] = make_int2((jj << sub_shift) + t, len - T * t < T ? len - T * t : T);
   lds_barrier();
   return __builtin_amdgcn_readfirstlane(total);
 }

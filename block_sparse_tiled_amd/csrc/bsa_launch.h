@@ -29,6 +29,7 @@ struct FwdProblem {
   float* ws;              // n_split_units partial slots (when splits > 1)
   int32_t* counters;      // one arrival counter per split item, zero between launches
   float* lse;             // [B, H, NT*T] log-sum-exp per row, or null
+  int32_t sub_shift;      // 1: the lists and lengths count tiles of 2*tile rows
 };
 
 // How the items are cut into work units, and the workspace that needs (none

@@ -20,7 +20,8 @@ FAKE = ctypes.c_void_p(0x1000)
 NUL = ctypes.c_void_p(0)
 
 LATENTS = [((21, 30, 52), (4, 4, 4)), ((5, 7, 9), (4, 4, 8)), ((3, 17, 33), (2, 8, 8)),
-           ((4, 4, 4), (4, 4, 4)), ((1, 1, 1), (4, 4, 4)), ((9, 1, 70), (1, 1, 64))]
+           ((4, 4, 4), (4, 4, 4)), ((1, 1, 1), (4, 4, 4)), ((9, 1, 70), (1, 1, 64)),
+           ((21, 30, 52), (4, 8, 8))]
 
 
 def test_hand_worked_example():
@@ -102,6 +103,7 @@ def test_cube_map_rejects_bad_arguments():
     assert lib.bsa_cube_tile_map(4, 4, 4, 4, 4, 4, 64, p, p, None) == INVALID
     assert lib.bsa_cube_tile_map(4, 4, 4, 4, 4, 2, 64, p, p, p) == INVALID  # 32 != 64
     assert lib.bsa_cube_tile_map(4, 4, 2, 4, 4, 2, 32, p, p, p) == SHAPE
+    assert lib.bsa_cube_tile_map(4, 8, 16, 4, 8, 16, 512, p, p, p) == SHAPE
     assert lib.bsa_cube_tile_map(4, -4, 4, 4, 4, 4, 64, p, p, p) == INVALID
     with pytest.raises(bsa.BsaError):
         bsa.cube_tile_map((4, 4, 4), (4, 4, 3))
@@ -115,6 +117,7 @@ def test_unlayout_rejects_bad_arguments():
     assert call(n=0) == INVALID
     assert call(n=5) == INVALID
     assert call(tile=96) == SHAPE
+    assert call(tile=512) == SHAPE
     assert call(D=32) == SHAPE
     assert call(m=NUL) == INVALID
     assert call(tok=-1) == INVALID

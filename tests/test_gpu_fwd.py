@@ -331,3 +331,32 @@ def test_split_lists_on_two_concurrent_streams(oracle_mod):
     ref = {"a": oracle_out(oracle_mod, wa), "b": oracle_out(oracle_mod, wb)}
     for name, out in outs:
         compare(bits_from_dev(out), ref[name], label=f"two streams {name}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_tile_256_random_lists(oracle_mod, D):
+    """256-row tiles: lengths above and below 128 (one or two non-empty halves), an
+    empty tile, long enough lists that the last round is split into segments."""
+    T = 256
+    vbs = [256, 200, 129, 128, 100, 0, 1, 256, 77, 250]
+    w = gen.random_problem(300 + D, B=1, H=3, D=D, T=T, vbs=vbs, density=0.7, pad="naninf")
+    print(f"fwd tile 256 D={D} NT={w.NT}", flush=True)
+    compare(run_fwd(w), oracle_out(oracle_mod, w), label=f"tile 256 D={D}")
+
+
+def test_tile_256_duplicates_and_lse(oracle_mod):
+    import oracle
+
+    T, D = 256, 128
+    w = gen.random_problem(310, B=2, H=1, D=D, T=T, vbs=[256, 130, 128, 3], counts=3, MS=3,
+                           duplicates=True)
+    w.q2k_num[1, 0, 2] = 0
+    print("fwd tile 256 duplicates + lse", flush=True)
+    q, k, v = (to_dev(x) for x in (w.q, w.k, w.v))
+    out, lse = bsa.fwd_lse(q, k, v, to_dev(w.q2k_idx), to_dev(w.q2k_num), to_dev(w.vbs), T)
+    compare(bits_from_dev(out), oracle_out(oracle_mod, w), label="tile 256 duplicates")
+    _, lse64 = oracle.fwd64(w.q, w.k, w.v, w.q2k_idx, w.q2k_num, w.vbs, T)
+    got = lse.cpu().numpy()
+    assert np.array_equal(np.isneginf(got), np.isneginf(lse64))
+    fin = np.isfinite(lse64)
+    np.testing.assert_allclose(got[fin], lse64[fin], rtol=1e-5, atol=1e-4)

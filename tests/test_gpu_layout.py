@@ -164,3 +164,17 @@ def test_cube_tiled_attention_layer_step(oracle_mod, T, cube):
     ref_tiled = oracle_mod.fwd(tq, tk, tv, idx, num, vbs, T)
     (ref,) = oracle_mod.tile_unlayout([ref_tiled], row)
     compare(bits_from_dev(got), ref, label=f"cube layer step T={T}")
+
+
+def test_tile_256_layout_and_unlayout(oracle_mod):
+    """256-row tiles from a 4 x 8 x 8 cube map of the video latent; both directions."""
+    rng = np.random.default_rng(256)
+    vbs, src, row = bsa.cube_tile_map((21, 30, 52), (4, 8, 8))
+    H, D, T = 2, 128, 256
+    x = rng.integers(0, 65536, size=(1, 21 * 30 * 52, H, D), dtype=np.uint16)
+    print("layout tile 256", flush=True)
+    (tiled,) = run_layout([x], src, T)
+    (want,) = oracle_mod.tile_layout([x], src, T)
+    np.testing.assert_array_equal(tiled, want)
+    (back,) = run_unlayout([tiled], row, T)
+    np.testing.assert_array_equal(back, x)
