@@ -18,8 +18,7 @@ LIB_PATH = os.path.join(HERE, "libbsa.so")
 MAX_BATCH_HEADS = 65535
 ROWS_LIMIT = 1 << 31
 TILES_LIMIT = 1 << 22
-TILES = (64, 128, 256)   # forward, layout; the backward takes 64 or 128
-BWD_TILES = (64, 128)
+TILES = (64, 128, 256)
 HEAD_DIMS = (64, 128)
 
 STATUS = {
@@ -364,8 +363,6 @@ def bwd(q, k, v, out, dout, lse, q2k_idx, q2k_num, k2q_idx, k2q_num, block_sizes
     import torch
 
     lib = load()
-    if tile not in BWD_TILES:
-        raise ValueError(f"the backward takes tiles of 64 or 128 rows, got {tile}")
     device, B, H, S, D, NT = _fwd_args(q, k, v, q2k_idx, q2k_num, block_sizes, tile)
     for t, name in ((out, "out"), (dout, "dout")):
         _require(t, name, torch.bfloat16, device, 4)

@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256) void delta_kernel(const uint16_t* __restrict__
                                                     const uint16_t* __restrict__ dout,
                                                     const int32_t* __restrict__ vbs, int num_tiles,
                                                     int tile, int64_t rows,
-                                                    float* __restrict__ delta) {
+                                                    float* __restrict__ delta, int sub_shift) {
   constexpr int kLanes = D / 8;  // lanes per row, 8 bf16 each
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int64_t row = gid / kLanes;
@@ -127,7 +127,8 @@ __global__ __launch_bounds__(256) void delta_kernel(const uint16_t* __restrict__
   if (row < rows) {
     const int64_t r = row % (static_cast<int64_t>(num_tiles) * tile);
     const int t = static_cast<int>(r / tile);
-    valid = static_cast<int>(r % tile) < clampi(vbs[t], 0, tile);
+    const int vq = clampi(vbs[t >> sub_shift] - tile * (t & ((1 << sub_shift) - 1)), 0, tile);
+    valid = static_cast<int>(r % tile) < vq;
     if (valid) {
       const uint4 o = *reinterpret_cast<const uint4*>(out + row * D + 8 * part);
       const uint4 g = *reinterpret_cast<const uint4*>(dout + row * D + 8 * part);
@@ -217,12 +218,12 @@ void dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                const float* __restrict__ lse, const float* __restrict__ delta,
                const int32_t* __restrict__ q2k_idx, const int32_t* __restrict__ q2k_num,
                const int32_t* __restrict__ vbs, uint16_t* __restrict__ dq, int num_tiles,
-               int max_sel, int n_items, int n_padded, float c, float scale) {
+               int max_sel, int n_items, int n_padded, float c, float scale, int sub_shift) {
   using C = Cfg<T, D>;
   constexpr int NDB = C::kDBlocks;
   __shared__ __attribute__((aligned(1024))) uint16_t ks[T * D];
   __shared__ __attribute__((aligned(1024))) uint16_t vs[T * D];
-  __shared__ int2 tl[C::kThreads];
+  __shared__ int2 tl[(T == 128 ? 2 : 1) * C::kThreads];  // two per entry with 2T-row lists
   __shared__ int wave_count[C::kWaves];
 
   const int item = item_of(blockIdx.x, n_padded);
@@ -239,9 +240,13 @@ void dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const uint16_t* kh = k + bh * head_elems;
   const uint16_t* vh = v + bh * head_elems;
   const int64_t row_g = (bh * num_tiles + tile_i) * T + qrow;  // this lane's query row
-  const int vq = clampi(vbs[tile_i], 0, T);
-  const int count = max_sel > 0 ? clampi(q2k_num[item], 0, max_sel) : 0;
-  const int32_t* list = q2k_idx + static_cast<int64_t>(item) * max_sel;
+  // lists and lengths count tiles of T << sub_shift rows (see the forward)
+  const int nt_list = num_tiles >> sub_shift;
+  const int tile_l = tile_i >> sub_shift;
+  const int64_t item_l = bh * nt_list + tile_l;
+  const int vq = clampi(vbs[tile_l] - T * (tile_i & ((1 << sub_shift) - 1)), 0, T);
+  const int count = max_sel > 0 ? clampi(q2k_num[item_l], 0, max_sel) : 0;
+  const int32_t* list = q2k_idx + item_l * max_sel;
 
   bf16x8_t qop[C::kKSteps], dop[C::kKSteps];
 #pragma unroll
@@ -262,8 +267,8 @@ void dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const f32x16_t zero16 = {};
 
   for (int base = 0; base < count; base += C::kThreads) {
-    const int total = compact_list<T, C::kWaves>(list, base, count, vbs, num_tiles, tl, wave_count,
-                                                 tid, wave, lane);
+    const int total = compact_list<T, C::kWaves>(list, base, count, vbs, nt_list, tl, wave_count,
+                                                 tid, wave, lane, sub_shift);
     if (total > 0) any_keys = true;
     for (int t = 0; t < total; ++t) {
       const int2 e = tl[t];
@@ -332,7 +337,8 @@ void dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 const float* __restrict__ lse, const float* __restrict__ delta,
                 const int32_t* __restrict__ k2q_idx, const int32_t* __restrict__ k2q_num,
                 const int32_t* __restrict__ vbs, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
-                int num_tiles, int max_k, int n_items, int n_padded, float c, float scale) {
+                int num_tiles, int max_k, int n_items, int n_padded, float c, float scale,
+                int sub_shift) {
   using C = Cfg<T, D>;
   constexpr int NDB = C::kDBlocks;
   // Q and dO tiles and their row statistics, double-buffered: the copies of
@@ -341,7 +347,7 @@ void dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   __shared__ __attribute__((aligned(1024))) uint16_t ds_all[2][T * D];  // dO tiles
   __shared__ __attribute__((aligned(16))) float lse_all[2][T];
   __shared__ __attribute__((aligned(16))) float dlt_all[2][T];
-  __shared__ int2 tl[C::kThreads];  // usable entries of the current list chunk: (tile, length)
+  __shared__ int2 tl[(T == 128 ? 2 : 1) * C::kThreads];  // usable entries: (tile, length)
   __shared__ int wave_count[C::kWaves];
 
   const int item = item_of(blockIdx.x, n_padded);  // (b*H + h) * NT + key tile j
@@ -358,9 +364,12 @@ void dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const uint16_t* qh = q + bh * head_elems;
   const uint16_t* oh = dout + bh * head_elems;
   const int64_t row_g = (bh * num_tiles + tile_j) * T + krow;  // this lane's key row
-  const int vk = clampi(vbs[tile_j], 0, T);
-  const int count = max_k > 0 ? clampi(k2q_num[item], 0, max_k) : 0;
-  const int32_t* list = k2q_idx + static_cast<int64_t>(item) * max_k;
+  const int nt_list = num_tiles >> sub_shift;
+  const int tile_l = tile_j >> sub_shift;
+  const int64_t item_l = bh * nt_list + tile_l;
+  const int vk = clampi(vbs[tile_l] - T * (tile_j & ((1 << sub_shift) - 1)), 0, T);
+  const int count = max_k > 0 ? clampi(k2q_num[item_l], 0, max_k) : 0;
+  const int32_t* list = k2q_idx + item_l * max_k;
 
   bf16x8_t kop[C::kKSteps], vop[C::kKSteps];
 #pragma unroll
@@ -398,8 +407,8 @@ void dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   };
 
   for (int base = 0; base < count; base += C::kThreads) {
-    const int total = compact_list<T, C::kWaves>(list, base, count, vbs, num_tiles, tl, wave_count,
-                                                 tid, wave, lane);
+    const int total = compact_list<T, C::kWaves>(list, base, count, vbs, nt_list, tl, wave_count,
+                                                 tid, wave, lane, sub_shift);
     if (total == 0) continue;
     wait_vmcnt<0>();  // the register operands loaded above
     issue(0, 0);
@@ -480,12 +489,12 @@ hipError_t launch_grads(const bsa::BwdProblem& p, hipStream_t stream) {
   dim3 block(Cfg<T, D>::kThreads);
   hipLaunchKernelGGL((dq_kernel<T, D>), dim3(n_padded), block, 0, stream, p.q, p.k, p.v, p.dout,
                      p.lse, p.delta, p.q2k_idx, p.q2k_num, p.block_sizes, p.dq, p.num_tiles,
-                     p.max_sel, n_items, n_padded, c, scale);
+                     p.max_sel, n_items, n_padded, c, scale, p.sub_shift);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((dkv_kernel<T, D>), dim3(n_padded), block, 0, stream, p.q, p.k, p.v, p.dout,
                      p.lse, p.delta, p.k2q_idx, p.k2q_num, p.block_sizes, p.dk, p.dv, p.num_tiles,
-                     p.max_k, n_items, n_padded, c, scale);
+                     p.max_k, n_items, n_padded, c, scale, p.sub_shift);
   return hipGetLastError();
 }
 
@@ -508,10 +517,12 @@ hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
   const int64_t blocks = (rows * lanes + 255) / 256;
   if (p.head_dim == 128)
     hipLaunchKernelGGL(delta_kernel<128>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
-                       p.out, p.dout, p.block_sizes, p.num_tiles, p.tile, rows, p.delta);
+                       p.out, p.dout, p.block_sizes, p.num_tiles, p.tile, rows, p.delta,
+                       p.sub_shift);
   else
     hipLaunchKernelGGL(delta_kernel<64>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
-                       p.out, p.dout, p.block_sizes, p.num_tiles, p.tile, rows, p.delta);
+                       p.out, p.dout, p.block_sizes, p.num_tiles, p.tile, rows, p.delta,
+                       p.sub_shift);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (p.tile == 128) return p.head_dim == 128 ? launch_grads<128, 128>(p, stream)

@@ -96,6 +96,7 @@ struct BwdProblem {
   int32_t max_k;
   int32_t tile;
   int32_t head_dim;
+  int32_t sub_shift;  // 1: the lists and lengths count tiles of 2*tile rows
 };
 
 hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream);

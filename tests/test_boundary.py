@@ -98,19 +98,20 @@ def test_fwd_rejects_unsupported_shapes(lib, tile, D):
     assert fwd_call(lib, tile=tile, D=D) == SHAPE
 
 
-def test_tile_256_is_a_forward_shape_but_not_a_backward_one(lib):
-    """256-row tiles pass validation in the forward (they fail only on reaching the
-    device check, or run); the backward refuses them."""
+def test_tile_256_passes_validation(lib):
+    """256-row tiles pass validation (they fail only on reaching the device check, or
+    run); 512 does not."""
     expected = {OK, NO_DEVICE, UNSUPPORTED}
     assert fwd_call(lib, tile=256, NT=0, ptr=NUL, idx=NUL) == OK
     assert fwd_call(lib, tile=256, D=64, B=64, H=64, NT=2048) == LIMITS  # rows = 2^31
     if not _device_present():
         assert fwd_call(lib, tile=256) in expected
     p = FAKE
-    assert lib.bsa_bwd(p, p, p, p, p, p, p, p, p, p, p, 256, p, p, p, p, 1, 1, 2, 128, 2, 2,
-                       NUL) == SHAPE
-    with pytest.raises(ValueError):
-        api.bwd(None, None, None, None, None, None, None, None, None, None, None, 256)
+    call = lambda tile: lib.bsa_bwd(p, p, p, p, p, p, p, p, p, p, p, tile, p, p, p, p, 1, 1, 2,  # noqa
+                                    128, 2, 2, NUL)
+    assert call(512) == SHAPE
+    if not _device_present():
+        assert call(256) in expected
 
 
 def test_fwd_rejects_bad_sizes_and_null_pointers(lib):

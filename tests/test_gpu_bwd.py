@@ -107,7 +107,7 @@ def check_problem(w, seed, label, max_k=None):
     compare_grad(got["dv"], dv, f"{label} dv")
 
 
-@pytest.mark.parametrize("T,D", [(64, 64), (64, 128), (128, 64), (128, 128)])
+@pytest.mark.parametrize("T,D", [(64, 64), (64, 128), (128, 64), (128, 128), (256, 64), (256, 128)])
 def test_random_ragged_lists(T, D):
     w = gen.random_problem(60 + T + D, B=1, H=2, D=D, T=T, vbs=[T, T - 5, 1, T, T // 2 + 3, T],
                            density=0.5, pad="nan")
@@ -187,3 +187,14 @@ def test_rising_logits():
         w.k[:, :, sl] = gen.to_bf16_bits(gen.bf16_bits_to_f32(w.k[:, :, sl]) * (0.25 + 0.25 * j))
     print("bwd rising logits", flush=True)
     check_problem(w, 7, "rising logits")
+
+
+def test_tile_256_duplicates_and_nan_padding():
+    """256-row tiles (run as 128-row halves): a tile listed twice, an empty list, lengths
+    on both sides of 128, NaN/Inf padding."""
+    T, D = 256, 128
+    w = gen.random_problem(95, B=2, H=1, D=D, T=T, vbs=[256, 129, 128, 40, 0], counts=3, MS=3,
+                           duplicates=True, pad="naninf")
+    w.q2k_num[1, 0, 1] = 0
+    print("bwd tile 256 duplicates", flush=True)
+    check_problem(w, 8, "tile 256 duplicates", max_k=3 * w.NT)
