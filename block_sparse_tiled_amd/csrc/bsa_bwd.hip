@@ -285,6 +285,7 @@ void dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       lds_barrier();
 #pragma unroll
       for (int hh = 0; hh < T / 64; ++hh) {  // 64 keys: key blocks 2*hh, 2*hh + 1
+        if (wave * 32 >= vq) break;  // every row of this wave is padding: nothing to compute
         f32x16_t s[2], dp[2];
 #pragma unroll
         for (int kk = 0; kk < C::kKSteps; ++kk)
@@ -433,6 +434,7 @@ void dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       if (t + 1 < total) issue(t + 1, buf ^ 1);
 #pragma unroll
     for (int qb = 0; qb < T / 32; ++qb) {
+      if (wave * 32 >= vk) break;  // every key row of this wave is padding
       f32x16_t s = zero16, dp = zero16;
 #pragma unroll
       for (int kk = 0; kk < C::kKSteps; ++kk) {

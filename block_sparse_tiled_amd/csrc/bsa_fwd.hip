@@ -163,6 +163,10 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   const int tile_l = tile_i >> sub_shift;
   const int64_t item_l = bh * nt_list + tile_l;
   const int count = max_sel > 0 ? clampi(q2k_num[item_l], 0, max_sel) : 0;
+  // A wave whose 32 query rows are all padding only copies and synchronises:
+  // its rows are written +0 whatever it computes (the other wave on its SIMD
+  // gets the issue slots).
+  const bool active = wave * 32 < clampi(vbs[tile_l] - T * (tile_i & ((1 << sub_shift) - 1)), 0, T);
   const int32_t* list = q2k_idx + item_l * max_sel;
   const int end = b < count ? b : count;
 
@@ -232,15 +236,17 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     //      operands of step kk + 1 requested before the MFMAs of step kk ----------
     f32x16_t s[NKB];
     bf16x8_t kop[2][NKB];  // operands of steps kk (kop[kk & 1]) and kk + 1, no copies
-    read_k(0, kop[0]);
+    if (active) {
+      read_k(0, kop[0]);
 #pragma unroll
-    for (int kk = 0; kk < C::kKSteps; ++kk) {
-      if (kk + 1 < C::kKSteps) read_k(kk + 1, kop[(kk + 1) & 1]);
+      for (int kk = 0; kk < C::kKSteps; ++kk) {
+        if (kk + 1 < C::kKSteps) read_k(kk + 1, kop[(kk + 1) & 1]);
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk & 1][kb], qop[kk],
-                                                        kk ? s[kb] : zero16, 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);  // keeps the reads one step ahead, no further
+        for (int kb = 0; kb < NKB; ++kb)
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk & 1][kb], qop[kk],
+                                                          kk ? s[kb] : zero16, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);  // keeps the reads one step ahead, no further
+      }
     }
     wait_vmcnt<0>();  // V(j) (the only copy in flight)
     if (vk < T) zero_padding_rows<T, D>(vs, vk, wave, lane);
@@ -248,6 +254,7 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     if (j2 >= 0) dma_tile<T, D, false>(kh + static_cast<int64_t>(j2) * T * D, ks, wave, k_dma);
 
     // ---- mask keys at or past vk (whole blocks included), running max ------------
+    if (active) {
     if (vk < 32 * NKB) {
       // register r of block kb holds key 32*kb + 8*(r/4) + r%4 (+ 4 in the high
       // half-wave): masked when 8*(r/4) + r%4 >= t = vk - 32*kb - 4*half, a
@@ -356,6 +363,7 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
 
     __builtin_amdgcn_s_setprio(0);
+    }  // active
 
     // ---- K(j2) landed (the only copy in flight); every wave is done with V(j) ------
     if (j2 >= 0) wait_vmcnt<0>();
