@@ -198,3 +198,40 @@ def test_tile_256_duplicates_and_nan_padding():
     w.q2k_num[1, 0, 1] = 0
     print("bwd tile 256 duplicates", flush=True)
     check_problem(w, 8, "tile 256 duplicates", max_k=3 * w.NT)
+
+
+def _head_slice(w, b, h):
+    """The problem restricted to one (batch, head): heads are independent in the
+    forward and the backward."""
+    import copy
+
+    s = copy.copy(w)
+    for name in ("q", "k", "v"):
+        setattr(s, name, getattr(w, name)[b:b + 1, h:h + 1].copy())
+    s.q2k_idx = w.q2k_idx[b:b + 1, h:h + 1].copy()
+    s.q2k_num = w.q2k_num[b:b + 1, h:h + 1].copy()
+    s.B, s.H = 1, 1
+    return s
+
+
+@pytest.mark.parametrize("name,heads", [("video", [(0, 0), (0, 5), (0, 11)]), ("stress", [(0, 0), (5, 7)]),
+                                        ("dense", [(0, 2)])])
+def test_full_size_config(name, heads):
+    """The full-size configurations, in the launch configuration the bench times:
+    the GPU runs the whole problem; sampled whole heads are compared with the oracle."""
+    import oracle
+
+    w = gen.make(name)
+    rng = np.random.default_rng(40)
+    dout = gen.to_bf16_bits(rng.standard_normal(w.q.shape).astype(np.float32))
+    print(f"bwd full size {name}: B={w.B} H={w.H} NT={w.NT}", flush=True)
+    got = run_all(w, dout)
+    pairs = list(heads)
+    if "neg_inf_row" in w.notes:  # the head holding the constructed all-(-inf) row
+        nb, nh, _ = w.notes["neg_inf_row"]
+        pairs.append((nb, nh))
+    for b, h in pairs:
+        s = _head_slice(w, b, h)
+        ref = oracle.bwd(s.q, s.k, s.v, dout[b:b + 1, h:h + 1], s.q2k_idx, s.q2k_num, s.vbs, s.T)
+        for key, r in zip(("dq", "dk", "dv"), ref):
+            compare_grad(got[key][b:b + 1, h:h + 1], r, f"{name} b{b} h{h} {key}")
