@@ -212,8 +212,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by batch*head with no exchange; see the design notes)",
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by batch*head with no exchange between GPUs)",
               file=sys.stderr)
         sys.exit(2)
 
