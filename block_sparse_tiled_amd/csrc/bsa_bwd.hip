@@ -275,8 +275,8 @@ void dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       const int j = __builtin_amdgcn_readfirstlane(e.x);
       const int vk = __builtin_amdgcn_readfirstlane(e.y);
       wait_vmcnt<0>();  // the operands loaded above
-      dma_tile<T, D, false>(kh + static_cast<int64_t>(j) * T * D, ks, wave, dl);
-      dma_tile<T, D, false>(vh + static_cast<int64_t>(j) * T * D, vs, wave, dl);
+      dma_tile<T, D, false, true>(kh + static_cast<int64_t>(j) * T * D, ks, wave, dl, vk);
+      dma_tile<T, D, false, true>(vh + static_cast<int64_t>(j) * T * D, vs, wave, dl, vk);
       wait_vmcnt<0>();
       if (vk < T) {
         zero_padding_rows<T, D>(ks, vk, wave, lane);
@@ -398,8 +398,8 @@ void dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const int i = __builtin_amdgcn_readfirstlane(e.x);
     const int vq = __builtin_amdgcn_readfirstlane(e.y);
     const int64_t qtile = static_cast<int64_t>(i) * T;
-    dma_tile<T, D, false>(qh + qtile * D, qs_all[buf], wave, dl);
-    dma_tile<T, D, false>(oh + qtile * D, ds_all[buf], wave, dl);
+    dma_tile<T, D, false, true>(qh + qtile * D, qs_all[buf], wave, dl, vq);
+    dma_tile<T, D, false, true>(oh + qtile * D, ds_all[buf], wave, dl, vq);
     if (tid < vq) {
       const int64_t r = (bh * num_tiles + i) * T + tid;
       l_next = lse[r];

@@ -229,7 +229,7 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   // blocks): keys at or past vk are masked, and a single step keeps the
   // accumulators in one register assignment across the loop (a second,
   // half-size step made the compiler move all of them every tile).
-  auto tile_step = [&](int vk, int j2) {
+  auto tile_step = [&](int vk, int j2, int vk2) {
     constexpr int NKB = C::kKeyBlocks;
 
     // ---- S^T = K_j Q^T, k-step outer: NKB independent accumulators, the
@@ -251,7 +251,7 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     wait_vmcnt<0>();  // V(j) (the only copy in flight)
     if (vk < T) zero_padding_rows<T, D>(vs, vk, wave, lane);
     lds_barrier();  // every wave is done with K(j); V(j) is visible
-    if (j2 >= 0) dma_tile<T, D, false>(kh + static_cast<int64_t>(j2) * T * D, ks, wave, k_dma);
+    if (j2 >= 0) dma_tile<T, D, false, true>(kh + static_cast<int64_t>(j2) * T * D, ks, wave, k_dma, vk2);
 
     // ---- mask keys at or past vk (whole blocks included), running max ------------
     if (active) {
@@ -368,7 +368,7 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     // ---- K(j2) landed (the only copy in flight); every wave is done with V(j) ------
     if (j2 >= 0) wait_vmcnt<0>();
     lds_barrier();
-    if (j2 >= 0) dma_tile<T, D, true>(vh + static_cast<int64_t>(j2) * T * D, vs, wave, v_dma);
+    if (j2 >= 0) dma_tile<T, D, true, true>(vh + static_cast<int64_t>(j2) * T * D, vs, wave, v_dma, vk2);
   };
 
   // Normalise and store the 32 x D rows of this wave (0 for padding query
@@ -426,8 +426,8 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     // are invisible to the compiler's wait-count bookkeeping, and an explicit
     // drain here keeps it from placing waits for Q inside the tile loop.
     wait_vmcnt<0>();
-    dma_tile<T, D, false>(kh + static_cast<int64_t>(j0) * T * D, ks, wave, k_dma);
-    dma_tile<T, D, true>(vh + static_cast<int64_t>(j0) * T * D, vs, wave, v_dma);
+    dma_tile<T, D, false>(kh + static_cast<int64_t>(j0) * T * D, ks, wave, k_dma, vk);
+    dma_tile<T, D, true>(vh + static_cast<int64_t>(j0) * T * D, vs, wave, v_dma, vk);
     wait_vmcnt<C::kDmaPerTile>();  // K(j0) has landed (V(j0) may be in flight)
     lds_barrier();
     for (int t = 0; t < total; ++t) {
@@ -437,7 +437,7 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         j2 = __builtin_amdgcn_readfirstlane(e.x);
         vk2 = __builtin_amdgcn_readfirstlane(e.y);
       }
-      tile_step(vk, j2);
+      tile_step(vk, j2, vk2);
       vk = vk2;
     }
   }

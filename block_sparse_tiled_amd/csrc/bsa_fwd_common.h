@@ -161,26 +161,46 @@ struct DmaLane {
   }
 };
 
-// Copy one T x D bf16 tile (rows at stride D from `src`) into `lds`, one
-// 1 KiB block per wave instruction (kDmaPerTile instructions per wave).
-// Instruction it of every wave moves both its global offset and its LDS
-// offset on by it * kWaves KiB, which is the scalar offset of the copy (and
-// added to M0); the rest of each address is a lane register of dl.
-// Buffer descriptor: base address, stride 0, size of one tile in bytes, and
-// the gfx9 word 3 for raw 32-bit data (data format 4 at bit 15).
-template <int T, int D, bool kIsV>
+// Copy the first `rows` rows (1 <= rows <= T) of a T x D bf16 tile (rows at
+// stride D from `src`) into `lds`, one 1 KiB block per wave instruction
+// (kDmaPerTile instructions per wave).  Instruction it of every wave moves
+// both its global offset and its LDS offset on by it * kWaves KiB, which is
+// the scalar offset of the copy (and added to M0); the rest of each address
+// is a lane register of dl.
+// Buffer descriptor: base address, stride 0, size of the `rows` rows in
+// bytes, and the gfx9 word 3 for raw 32-bit data (data format 4 at bit 15).
+// Lanes whose 16 bytes lie past that size fail the range check: they read
+// nothing from memory and never fault, so the padding rows of a short tile
+// cost no memory traffic.  What such a lane leaves in LDS is not relied on:
+// K padding keys are masked by select and V padding rows are zeroed after
+// the copy lands.
+//
+// With kSkipPadding, a wave also skips the instructions whose whole block lies
+// past `rows` (a uniform test), so it issues fewer than kDmaPerTile copies:
+// only for copies that are waited for with vmcnt(0).
+template <int T, int D, bool kIsV, bool kSkipPadding = false>
 __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, uint16_t* lds,
-                                         int wave, const DmaLane<T, D, kIsV>& dl) {
+                                         int wave, const DmaLane<T, D, kIsV>& dl, int rows = T) {
   using C = Cfg<T, D>;
   using DL = DmaLane<T, D, kIsV>;
   const uint32_t base = launder_s(__builtin_amdgcn_readfirstlane(lds_address(lds)) + wave * 1024);
   const uint64_t g = reinterpret_cast<uintptr_t>(src);
   const i32x4_t srd = {static_cast<int>(static_cast<uint32_t>(g)),
-                       static_cast<int>(static_cast<uint32_t>(g >> 32)), T * D * 2, 0x00020000};
+                       static_cast<int>(static_cast<uint32_t>(g >> 32)), rows * D * 2, 0x00020000};
+  if (!kSkipPadding || rows >= T) {
 #pragma unroll
-  for (int it = 0; it < C::kDmaPerTile; ++it) {
-    const uint32_t soff = it * C::kWaves * 1024;
-    dma16(srd, dl.off[it % DL::kN], soff, base + soff);
+    for (int it = 0; it < C::kDmaPerTile; ++it) {
+      const uint32_t soff = it * C::kWaves * 1024;
+      dma16(srd, dl.off[it % DL::kN], soff, base + soff);
+    }
+  } else {
+    constexpr int kRowsPerBlock = 512 / D;  // rows in one 1 KiB block
+#pragma unroll
+    for (int it = 0; it < C::kDmaPerTile; ++it) {
+      if ((it * C::kWaves + wave) * kRowsPerBlock >= rows) break;
+      const uint32_t soff = it * C::kWaves * 1024;
+      dma16(srd, dl.off[it % DL::kN], soff, base + soff);
+    }
   }
 }
 
