@@ -432,43 +432,64 @@ void dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       }
       lds_barrier();  // tile t visible; every wave is done with tile t - 1's buffer
       if (t + 1 < total) issue(t + 1, buf ^ 1);
-#pragma unroll
-    for (int qb = 0; qb < T / 32; ++qb) {
-      if (wave * 32 >= vk) break;  // every key row of this wave is padding
-      f32x16_t s = zero16, dp = zero16;
-#pragma unroll
-      for (int kk = 0; kk < C::kKSteps; ++kk) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows<D>(qs, 32 * qb, kk, col, half), kop[kk],
-                                                    kk ? s : zero16, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows<D>(ds_, 32 * qb, kk, col, half), vop[kk],
-                                                     kk ? dp : zero16, 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // register r holds query 32*qb + 8*(r/4) + 4*half + r%4: statistics four at a time
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 l4 = *reinterpret_cast<const float4*>(lse_s + 32 * qb + 8 * g + 4 * half);
-        const float4 d4 = *reinterpret_cast<const float4*>(dlt_s + 32 * qb + 8 * g + 4 * half);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lv[e]));
-          s[r] = p;                      // P
-          dp[r] = p * (dp[r] - dv4[e]);  // dS
+    // Per 32-query block: S = Q K^T and dP = dO V^T (steps k < NA), P and dS,
+    // then dV^T += dO^T P and dK^T += Q^T dS over its two 16-query chunks
+    // (steps k >= NA).  With one wave per SIMD nothing hides LDS latency but
+    // the wave's own MFMAs, so the two LDS operands of every step are read
+    // kAhead steps early, through a ring of registers, across blocks and
+    // phases.  A wave whose key rows are all padding skips the compute.
+    if (wave * 32 < vk) {
+      constexpr int NQB = T / 32, NA = C::kKSteps, NS = NA + 2 * NDB, kSteps = NQB * NS;
+      constexpr int kAhead = 3, kRing = kAhead + 1;
+      bf16x8_t ra[kRing], rb[kRing];
+      auto load = [&](int st) {
+        const int qb = st / NS, k = st % NS, sl = st % kRing;
+        if (k < NA) {
+          ra[sl] = read_rows<D>(qs, 32 * qb, k, col, half);
+          rb[sl] = read_rows<D>(ds_, 32 * qb, k, col, half);
+        } else {
+          const int cc = (k - NA) / NDB, db = (k - NA) % NDB;
+          ra[sl] = read_rows_t<D>(ds_, 2 * qb + cc, db, lane);
+          rb[sl] = read_rows_t<D>(qs, 2 * qb + cc, db, lane);
         }
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS over the two 16-query chunks of this block
+      };
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const bf16x8_t pb = pack8(s, 8 * cc);
-        const bf16x8_t sb = pack8(dp, 8 * cc);
+      for (int st = 0; st < kAhead; ++st) load(st);
+      f32x16_t s = zero16, dp = zero16;
+      bf16x8_t pb[2], sb[2];
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          accv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows_t<D>(ds_, 2 * qb + cc, db, lane),
-                                                             pb, accv[db], 0, 0, 0);
-          acck[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows_t<D>(qs, 2 * qb + cc, db, lane),
-                                                             sb, acck[db], 0, 0, 0);
+      for (int st = 0; st < kSteps; ++st) {
+        if (st + kAhead < kSteps) load(st + kAhead);
+        const int qb = st / NS, k = st % NS, sl = st % kRing;
+        if (k < NA) {
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[sl], kop[k], k ? s : zero16, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rb[sl], vop[k], k ? dp : zero16, 0, 0, 0);
+        } else {
+          const int cc = (k - NA) / NDB, db = (k - NA) % NDB;
+          accv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[sl], pb[cc], accv[db], 0, 0, 0);
+          acck[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rb[sl], sb[cc], acck[db], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (k == NA - 1) {
+          // register r holds query 32*qb + 8*(r/4) + 4*half + r%4: statistics four at a time
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float4 l4 = *reinterpret_cast<const float4*>(lse_s + 32 * qb + 8 * g + 4 * half);
+            const float4 d4 = *reinterpret_cast<const float4*>(dlt_s + 32 * qb + 8 * g + 4 * half);
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * g + e;
+              const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lv[e]));
+              s[r] = pr;                      // P
+              dp[r] = pr * (dp[r] - dv4[e]);  // dS
+            }
+          }
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc) {
+            pb[cc] = pack8(s, 8 * cc);
+            sb[cc] = pack8(dp, 8 * cc);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
