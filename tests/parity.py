@@ -13,6 +13,9 @@ from block_sparse_tiled_amd import inputs as gen
 
 MAX_ABS = 2e-2
 MEAN_ABS = 2e-3
+# gradients: the same bar on the gradients' own scale, max(1, RMS of the oracle's values)
+MAX_REL = 2e-2
+MEAN_REL = 2e-3
 
 
 def to_dev(a, device="cuda"):
@@ -80,3 +83,42 @@ def sample_rows(w, n, rng, extra=()):
                      bh * S + S - 1])
     rows.update(int(x) for x in extra)
     return np.array(sorted(r for r in rows if 0 <= r < total), np.int64)
+
+
+def compare_grad(got_bits, ref, label):
+    """Gradients (bf16 on the GPU) against the fp64 oracle.
+
+    NaN and Inf positions identical; rows the oracle leaves at exactly 0 are +0
+    bit for bit; with s = max(1, RMS of the oracle's finite values), every
+    element within 2e-2 s + 2^-7 max(|ref|, RMS of its row), and the mean
+    difference within 2e-3 s.  The second term is a bf16 ulp of the larger of
+    the value and its row's scale: the result is bf16, and P and dS enter the
+    products as bf16, so each row carries rounding noise of relative size
+    2^-9 sqrt(n) over its n terms, as large as the row itself is (a row's
+    values are sums of n terms of either sign).  It matters only where a key
+    tile is listed by very many query tiles and its gradients stand far above s.
+    """
+    got = gen.bf16_bits_to_f32(got_bits).astype(np.float64)
+    nan_ref, nan_got = np.isnan(ref), np.isnan(got)
+    assert np.array_equal(nan_ref, nan_got), (
+        f"{label}: NaN mask differs ({int(nan_ref.sum())} oracle, {int(nan_got.sum())} GPU)")
+    zero_rows = np.all(ref == 0, axis=-1)
+    assert np.all(got_bits[zero_rows] == 0), f"{label}: rows the oracle leaves at 0 are not +0"
+    fin = np.isfinite(ref) & ~nan_ref
+    assert np.array_equal(np.isinf(got), np.isinf(ref)), f"{label}: Inf mask differs"
+    diff = np.abs(got[fin] - ref[fin])
+    s = max(1.0, float(np.sqrt(np.mean(ref[fin] ** 2)))) if fin.any() else 1.0
+    fin_ref = np.where(fin, ref, 0.0)
+    row_rms = np.sqrt(np.mean(fin_ref ** 2, axis=-1, keepdims=True))
+    bar = MAX_REL * s + 2.0 ** -7 * np.maximum(np.abs(fin_ref), row_rms)[fin]
+    over = diff > bar
+    mx = float(diff.max()) if diff.size else 0.0
+    mean = float(diff.mean()) if diff.size else 0.0
+    print(f"{label}: max {mx:.3e} mean {mean:.3e} (scale {s:.3f})", flush=True)
+    if over.any():  # where the worst elements are, for the failure message
+        idx = np.argwhere(fin)[over][:5]
+        worst = [(tuple(int(x) for x in w), float(ref[tuple(w)]), float(got[tuple(w)])) for w in idx]
+        print(f"{label}: {int(over.sum())} elements over the bar; first (index, oracle, GPU): {worst}",
+              flush=True)
+    assert not over.any() and mean <= MEAN_REL * s, f"{label}: max {mx:.3e} mean {mean:.3e} scale {s:.3f}"
+    return mx / s, mean / s

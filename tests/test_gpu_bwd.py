@@ -4,23 +4,21 @@ bsa_bwd) against the fp64 oracle (oracle.bsa_bwd), through the C ABI.
 Compare rule for gradients (bf16 on the GPU, fp64 in the oracle): NaN
 positions identical; rows the oracle leaves at exactly 0 (padding rows, rows in
 no listed pair) are +0 bit for bit; over the other elements, with s =
-max(1, RMS of the oracle's finite values), max |diff| <= 2e-2 s and mean |diff|
-<= 2e-3 s: the forward's bar, on the gradients' own scale.  (Measured on the
-random and config shapes: max about 5e-3, mean about 2e-4.)  The transposed
-lists are compared bit for bit.
+max(1, RMS of the oracle's finite values), |diff| <= 2e-2 s + 2^-7 |oracle| per
+element and mean |diff| <= 2e-3 s: the forward's bar on the gradients' own
+scale, plus one bf16 ulp of each value, which matters only where a key tile's
+gradients stand far above s (parity.compare_grad).  (Measured on the random and
+config shapes: max about 5e-3, mean about 2e-4.)  The transposed lists are
+compared bit for bit.
 """
 import numpy as np
 import pytest
 
 import block_sparse_tiled_amd as bsa
 from block_sparse_tiled_amd import inputs as gen
-from parity import bits_from_dev, to_dev
+from parity import bits_from_dev, compare_grad, to_dev
 
 pytestmark = pytest.mark.gpu
-
-MAX_REL = 2e-2
-MEAN_REL = 2e-3
-
 
 @pytest.fixture(scope="module", autouse=True)
 def gpu():
@@ -56,24 +54,6 @@ def run_all(w, dout_bits, max_k=None):
     return {"out": bits_from_dev(out), "lse": lse.cpu().numpy(), "dq": bits_from_dev(dq),
             "dk": bits_from_dev(dk), "dv": bits_from_dev(dv),
             "k2q_idx": k2q_idx.cpu().numpy(), "k2q_num": k2q_num.cpu().numpy()}
-
-
-def compare_grad(got_bits, ref, label):
-    got = gen.bf16_bits_to_f32(got_bits).astype(np.float64)
-    nan_ref, nan_got = np.isnan(ref), np.isnan(got)
-    assert np.array_equal(nan_ref, nan_got), (
-        f"{label}: NaN mask differs ({int(nan_ref.sum())} oracle, {int(nan_got.sum())} GPU)")
-    zero_rows = np.all(ref == 0, axis=-1)
-    assert np.all(got_bits[zero_rows] == 0), f"{label}: rows the oracle leaves at 0 are not +0"
-    fin = np.isfinite(ref) & ~nan_ref
-    assert np.array_equal(np.isinf(got), np.isinf(ref)), f"{label}: Inf mask differs"
-    diff = np.abs(got[fin] - ref[fin])
-    s = max(1.0, float(np.sqrt(np.mean(ref[fin] ** 2)))) if fin.any() else 1.0
-    mx = float(diff.max()) if diff.size else 0.0
-    mean = float(diff.mean()) if diff.size else 0.0
-    print(f"{label}: max {mx:.3e} mean {mean:.3e} (scale {s:.3f})", flush=True)
-    assert mx <= MAX_REL * s and mean <= MEAN_REL * s, f"{label}: max {mx:.3e} mean {mean:.3e} scale {s:.3f}"
-    return mx / s, mean / s
 
 
 def check_problem(w, seed, label, max_k=None):
