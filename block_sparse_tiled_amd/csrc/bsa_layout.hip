@@ -26,8 +26,12 @@ struct Ptrs {
   uint4* dst[4];
 };
 
-// D8 = 16-byte chunks per row (8 for D = 64, 16 for D = 128).
-template <int D8>
+// D8 = 16-byte chunks per row (8 for D = 64, 16 for D = 128).  Each thread
+// moves one chunk per step, or, for small launches (U = 4), four chunks 256
+// apart with all loads before the stores: fewer, fuller workgroups finish
+// sooner there (measured: the 12-head, 8192-row ragged shape 33.4 -> 31.1
+// us), while the larger shapes ran 1-2 % slower that way.
+template <int D8, int U>
 __global__ __launch_bounds__(256) void tile_layout_kernel(Ptrs p, int n_tensors,
                                                           const int32_t* __restrict__ map,
                                                           int64_t tokens, int64_t heads,
@@ -36,23 +40,46 @@ __global__ __launch_bounds__(256) void tile_layout_kernel(Ptrs p, int n_tensors,
   const int64_t b = bh / heads;
   const int64_t h = bh - b * heads;
   const int64_t chunks = rows_per_head * D8;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  for (int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; c < chunks;
-       c += stride) {
-    const int64_t t = c / D8;
-    const int ch = static_cast<int>(c % D8);
-    const int32_t s = map[t];
-    const int64_t out_off = bh * chunks + c;
-    if (s >= 0 && s < tokens) {
-      const int64_t in_off = ((b * tokens + s) * heads + h) * D8 + ch;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x * U;
+  if constexpr (U == 1) {
+    for (int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; c < chunks;
+         c += stride) {
+      const int32_t s = map[c / D8];
+      const int64_t out_off = bh * chunks + c;
+      if (s >= 0 && s < tokens) {
+        const int64_t in_off = ((b * tokens + s) * heads + h) * D8 + c % D8;
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          if (x < n_tensors) p.dst[x][out_off] = p.src[x][in_off];
+      } else {
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          if (x < n_tensors) p.dst[x][out_off] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+    return;
+  }
+  for (int64_t c0 = static_cast<int64_t>(blockIdx.x) * blockDim.x * U + threadIdx.x; c0 < chunks;
+       c0 += stride) {
+    uint4 val[U][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = c0 + u * 256;
+      const int32_t s = c < chunks ? map[c / D8] : -1;
+      const bool ok = s >= 0 && s < tokens;
+      const int64_t in_off = ((b * tokens + (ok ? s : 0)) * heads + h) * D8 + c % D8;
 #pragma unroll
       for (int x = 0; x < 4; ++x)
-        if (x < n_tensors) p.dst[x][out_off] = p.src[x][in_off];
-    } else {
-      const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+        val[u][x] = x < n_tensors && ok ? p.src[x][in_off] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = c0 + u * 256;
+      if (c >= chunks) break;
+      const int64_t out_off = bh * chunks + c;
 #pragma unroll
       for (int x = 0; x < 4; ++x)
-        if (x < n_tensors) p.dst[x][out_off] = zero;
+        if (x < n_tensors) p.dst[x][out_off] = val[u][x];
     }
   }
 }
@@ -103,7 +130,9 @@ hipError_t launch_tile_layout(const LayoutProblem& lp, hipStream_t stream) {
   }
   const int d8 = lp.head_dim / 8;
   const int64_t chunks = lp.rows_per_head * d8;
-  const int64_t want = (chunks + 255) / 256;
+  const bool small = chunks * lp.batch * lp.heads < (int64_t{1} << 21);
+  const int u = small ? 4 : 1;
+  const int64_t want = (chunks + 256 * u - 1) / (256 * u);
   dim3 grid(static_cast<unsigned>(want < 65536 ? want : 65536),
             static_cast<unsigned>(lp.batch * lp.heads));
   dim3 block(256);
@@ -111,8 +140,11 @@ hipError_t launch_tile_layout(const LayoutProblem& lp, hipStream_t stream) {
   const int32_t* map = lp.tile_src_token;
   int64_t tokens = lp.tokens, heads = lp.heads, rows = lp.rows_per_head;
   void* args[] = {&p, &n, &map, &tokens, &heads, &rows};
-  const void* fn = d8 == 16 ? reinterpret_cast<const void*>(&tile_layout_kernel<16>)
-                            : reinterpret_cast<const void*>(&tile_layout_kernel<8>);
+  const void* fn =
+      d8 == 16 ? (small ? reinterpret_cast<const void*>(&tile_layout_kernel<16, 4>)
+                        : reinterpret_cast<const void*>(&tile_layout_kernel<16, 1>))
+               : (small ? reinterpret_cast<const void*>(&tile_layout_kernel<8, 4>)
+                        : reinterpret_cast<const void*>(&tile_layout_kernel<8, 1>));
   return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 
