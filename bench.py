@@ -71,6 +71,22 @@ def load_traffic(workload):
     return rec.get("fwd_bytes_per_launch")
 
 
+def run_env(dev):
+    """The device and software the numbers were taken on."""
+    import torch
+
+    props = torch.cuda.get_device_properties(dev)
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    return {"device": props.name, "arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "rocm": rocm,
+            "torch": torch.__version__, "hip": torch.version.hip}
+
+
 def cpu_threads():
     try:
         n = len(os.sched_getaffinity(0))
@@ -207,6 +223,9 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time the training pass instead: log-sum-exp forward, transposed lists, "
                          "backward (prints its own JSON line)")
+    ap.add_argument("--cold", type=int, default=0,
+                    help="also time this many forward calls, each after a 1 GiB scratch write "
+                         "(cache-cold; off by default so that profiles count only the timed steps)")
     ap.add_argument("--fwd-only", action="store_true",
                     help="time only the attention launch (no layout) -- for profiling")
     args = ap.parse_args()
@@ -302,6 +321,20 @@ def main():
     torch.cuda.synchronize()
     unlayout_ms = un_ev[0].elapsed_time(un_ev[1]) / n_un
     unlayout_bytes = 2 * 2 * w.D * w.B * w.H * tokens + 4 * tokens
+
+    cold_ms = None
+    if args.cold > 0:
+        # forward calls after a 1 GiB scratch write each, which evicts L2 and MALL
+        scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        cold_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.cold)]
+        for c in range(args.cold):
+            scratch.fill_(float(c))
+            cold_ev[c][0].record(stream)
+            bsa.fwd(tiled[0], tiled[1], tiled[2], idx, num, vbs, w.T, out=out)
+            cold_ev[c][1].record(stream)
+        torch.cuda.synchronize()
+        cold_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in cold_ev]))
+        del scratch
     rec = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -327,6 +360,8 @@ def main():
         "pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_ms": round(fwd_avg, 5),
         "fwd_ms_min": round(float(np.min(fwd_ms)), 5),
+        "fwd_ms_median": round(float(np.median(fwd_ms)), 5),
+        "fwd_ms_cold": round(cold_ms, 5) if cold_ms is not None else None,
         "layout_ms": round(float(np.mean(lay_ms)), 5),
         "layout_gbs": (round(layout_bytes / (float(np.mean(lay_ms)) * 1e-3) / 1e9, 1)
                        if not args.fwd_only else None),
@@ -346,6 +381,7 @@ def main():
             "traffic": traffic,
         },
         "kernel_source_digest": kernel_source_digest(),
+        "env": run_env(dev),
     }
     if args.calibrate_copy:
         # a plain elementwise copy of known size: reads and writes 1 GiB once
