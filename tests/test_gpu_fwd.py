@@ -333,6 +333,29 @@ def test_split_lists_on_two_concurrent_streams(oracle_mod):
         compare(bits_from_dev(out), ref[name], label=f"two streams {name}")
 
 
+def test_split_lists_on_many_streams(oracle_mod):
+    """A device keeps at most eight stream workspaces; on further streams a launch
+    that would split its lists runs whole query tiles instead.  Twelve streams,
+    each used twice (concurrently with the others), all match the oracle."""
+    import torch
+
+    w = gen.random_problem(65, B=1, H=2, D=128, T=128, vbs=[128] * 20 + [90], density=0.8)
+    args = _launch_args(w)
+    streams = [torch.cuda.Stream() for _ in range(12)]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(2):
+        for s in streams:
+            with torch.cuda.stream(s):
+                outs.append(bsa.fwd(*args, w.T))
+    for s in streams:
+        s.synchronize()
+    ref = oracle_out(oracle_mod, w)
+    for n, out in enumerate(outs):
+        compare(bits_from_dev(out), ref, label=f"stream {n % len(streams)}")
+
+
 @pytest.mark.parametrize("D", [64, 128])
 def test_tile_256_random_lists(oracle_mod, D):
     """256-row tiles: lengths above and below 128 (one or two non-empty halves), an
