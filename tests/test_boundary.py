@@ -89,8 +89,24 @@ FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails val
 NUL = ctypes.c_void_p(0)
 
 
-def fwd_call(lib, tile=128, D=128, B=1, H=1, NT=2, MS=2, ptr=FAKE, idx=FAKE):
-    return lib.bsa_fwd(ptr, ptr, ptr, idx, ptr, ptr, tile, ptr, B, H, NT, D, MS, NUL)
+def fake(i):
+    """Distinct fake device addresses, 256 MiB apart (never dereferenced)."""
+    return ctypes.c_void_p((i + 1) << 28)
+
+
+def fwd_call(lib, tile=128, D=128, B=1, H=1, NT=2, MS=2, ptr=None, idx=None, out=None):
+    q, k, v, num, bs = ((ptr if ptr is not None else fake(i)) for i in range(5))
+    idx = fake(5) if idx is None else idx
+    out = (ptr if ptr is not None else fake(6)) if out is None else out
+    return lib.bsa_fwd(q, k, v, idx, num, bs, tile, out, B, H, NT, D, MS, NUL)
+
+
+def bwd_call(lib, tile=128, outs=None, ins=None):
+    """bsa_bwd on a 1 x 1 x 2-tile problem with fake pointers (inputs 0..10, outputs 11..14)."""
+    i = [fake(n) for n in range(11)] if ins is None else ins
+    o = [fake(11 + n) for n in range(4)] if outs is None else outs
+    return lib.bsa_bwd(i[0], i[1], i[2], i[3], i[4], i[5], i[6], i[7], i[8], i[9], i[10], tile,
+                       o[0], o[1], o[2], o[3], 1, 1, 2, 128, 2, 2, NUL)
 
 
 @pytest.mark.parametrize("tile,D", [(32, 128), (512, 128), (128, 96), (64, 256), (0, 64), (192, 64)])
@@ -106,12 +122,42 @@ def test_tile_256_passes_validation(lib):
     assert fwd_call(lib, tile=256, D=64, B=64, H=64, NT=2048) == LIMITS  # rows = 2^31
     if not _device_present():
         assert fwd_call(lib, tile=256) in expected
-    p = FAKE
-    call = lambda tile: lib.bsa_bwd(p, p, p, p, p, p, p, p, p, p, p, tile, p, p, p, p, 1, 1, 2,  # noqa
-                                    128, 2, 2, NUL)
-    assert call(512) == SHAPE
+    assert bwd_call(lib, 512) == SHAPE
     if not _device_present():
-        assert call(256) in expected
+        assert bwd_call(lib, 256) in expected
+
+
+def test_outputs_that_overlap_inputs_are_refused(lib):
+    """An output sharing bytes with an input or another output is INVALID_ARGUMENT
+    (checked on the host before any launch); inputs may share memory."""
+    expected = {OK, NO_DEVICE, UNSUPPORTED}
+    assert fwd_call(lib, out=fake(0)) == INVALID  # out is q
+    # out starts inside v: [1, 1, 256, 128] bf16 is 64 KiB
+    assert fwd_call(lib, out=ctypes.c_void_p(fake(2).value + 65534)) == INVALID
+    assert fwd_call(lib, out=ctypes.c_void_p(fake(2).value + 65536)) in expected  # just past v
+    assert fwd_call(lib, idx=ctypes.c_void_p(fake(6).value + 8)) == INVALID  # out over the list
+    q = fake(0)
+    # q, k and v may be one tensor
+    assert lib.bsa_fwd(q, q, q, fake(5), fake(3), fake(4), 128, fake(6), 1, 1, 2, 128, 2,
+                       NUL) in expected
+    lse_on_out = ctypes.c_void_p(fake(6).value + 100)
+    assert lib.bsa_fwd_lse(q, q, q, fake(5), fake(3), fake(4), 128, fake(6), lse_on_out, 1, 1, 2,
+                           128, 2, NUL) == INVALID
+    # backward: dk on dq, delta on dout, dv on the transposed lists
+    o = [fake(11 + n) for n in range(4)]
+    assert bwd_call(lib, outs=[o[0], o[0], o[2], o[3]]) == INVALID
+    assert bwd_call(lib, outs=[o[0], o[1], o[2], fake(4)]) == INVALID
+    assert bwd_call(lib, outs=[o[0], o[1], fake(8), o[3]]) == INVALID
+    if not _device_present():
+        assert bwd_call(lib) in expected
+    # layout and its inverse: a destination on a source or on the map
+    src = (ctypes.c_void_p * 2)(fake(0), fake(1))
+    dst = (ctypes.c_void_p * 2)(fake(2), fake(0))
+    assert lib.bsa_tile_layout(src, dst, 2, fake(4), 64, 1, 64, 1, 1, 64, NUL) == INVALID
+    dst = (ctypes.c_void_p * 2)(fake(2), fake(4))
+    assert lib.bsa_tile_layout(src, dst, 2, fake(4), 64, 1, 64, 1, 1, 64, NUL) == INVALID
+    dst = (ctypes.c_void_p * 2)(fake(2), fake(2))
+    assert lib.bsa_tile_unlayout(src, dst, 2, fake(4), 64, 1, 64, 1, 1, 64, NUL) == INVALID
 
 
 def test_fwd_rejects_bad_sizes_and_null_pointers(lib):
@@ -128,9 +174,10 @@ def test_fwd_rejects_bad_sizes_and_null_pointers(lib):
 
 
 def test_layout_rejects_bad_arguments(lib):
-    arr = (ctypes.c_void_p * 4)(FAKE, FAKE, FAKE, FAKE)
-    call = lambda n=1, tile=64, D=64, B=1, H=1, NT=1, tok=64, m=FAKE: lib.bsa_tile_layout(  # noqa
-        arr, arr, n, m, tile, B, tok, H, NT, D, NUL)
+    srcs = (ctypes.c_void_p * 4)(*[fake(n) for n in range(4)])
+    dsts = (ctypes.c_void_p * 4)(*[fake(4 + n) for n in range(4)])
+    call = lambda n=1, tile=64, D=64, B=1, H=1, NT=1, tok=64, m=fake(9): lib.bsa_tile_layout(  # noqa
+        srcs, dsts, n, m, tile, B, tok, H, NT, D, NUL)
     assert call(n=0) == INVALID
     assert call(n=5) == INVALID
     assert call(tile=96) == SHAPE
@@ -143,9 +190,9 @@ def test_layout_rejects_bad_arguments(lib):
 @pytest.mark.skipif("_device_present()", reason="checks the no-device path; a GPU is visible")
 def test_without_a_device_launches_fail_cleanly(lib):
     assert fwd_call(lib) == NO_DEVICE
-    arr = (ctypes.c_void_p * 1)(FAKE)
-    assert lib.bsa_tile_layout(arr, arr, 1, FAKE, 64, 1, 64, 1, 1, 64, NUL) == NO_DEVICE
-    assert lib.bsa_tile_unlayout(arr, arr, 1, FAKE, 64, 1, 64, 1, 1, 64, NUL) == NO_DEVICE
+    src, dst = (ctypes.c_void_p * 1)(fake(0)), (ctypes.c_void_p * 1)(fake(1))
+    assert lib.bsa_tile_layout(src, dst, 1, fake(2), 64, 1, 64, 1, 1, 64, NUL) == NO_DEVICE
+    assert lib.bsa_tile_unlayout(src, dst, 1, fake(2), 64, 1, 64, 1, 1, 64, NUL) == NO_DEVICE
     import torch
 
     # a CPU tensor is refused: there is no CPU implementation to fall back on
