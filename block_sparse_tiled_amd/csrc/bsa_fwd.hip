@@ -308,7 +308,8 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 
 
     // ---- per 16-key chunk: P = exp2(S*c - m*c) in bf16, row sum, O^T += V^T P^T.
-    //      Every chunk of the tile is processed: keys at or past vk have p = 0
+    //      Every chunk up to the one holding key vk - 1 is processed, and the
+    //      whole second half unless vk <= T/2: keys at or past vk have p = 0
     //      and zeroed V rows, so they add exact zeros.  Software-pipelined: the
     //      exponentials of chunk kc + 1 and the V operand reads of chunk kc + 1
     //      are interleaved with the four MFMAs of chunk kc (one MFMA, then two
@@ -360,6 +361,10 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
       }
       __builtin_amdgcn_sched_barrier(0);
       pk = pk_next;
+      // A tile whose valid keys all lie in its first half stops here.  (One exit
+      // point only: an exit after every chunk made the compiler drain the LDS
+      // reads in flight at each one, 2-6 % slower on full tiles.)
+      if (kc == NKB - 1 && 16 * (kc + 1) >= vk) break;
     }
 
     __builtin_amdgcn_s_setprio(0);
