@@ -116,6 +116,28 @@ def test_ragged_config_every_row():
     check_problem(w, 4, "ragged")
 
 
+def test_zero_width_lists():
+    """max_sel = 0 (an index tensor with no columns, passed as a null pointer): the
+    forward gives +0 rows and -inf log-sum-exp, the lists are empty, the gradients +0."""
+    import torch
+
+    rng = np.random.default_rng(77)
+    B, H, T, D, NT = 1, 2, 128, 128, 3
+    x = [gen.to_bf16_bits(rng.standard_normal((B, H, NT * T, D)).astype(np.float32)) for _ in range(4)]
+    q, k, v, dout = (to_dev(a) for a in x)
+    idx = torch.zeros((B, H, NT, 0), dtype=torch.int32, device="cuda")
+    num = torch.zeros((B, H, NT), dtype=torch.int32, device="cuda")
+    vbs = to_dev(np.array([T, 77, T], np.int32))
+    out, lse = bsa.fwd_lse(q, k, v, idx, num, vbs, T)
+    k2q_idx, k2q_num = bsa.bwd_k2q(idx, num)
+    dq, dk, dv = bsa.bwd(q, k, v, out, dout, lse, idx, num, k2q_idx, k2q_num, vbs, T)
+    torch.cuda.synchronize()
+    for name, t in (("out", out), ("dq", dq), ("dk", dk), ("dv", dv)):
+        assert np.all(bits_from_dev(t) == 0), f"{name} is not +0 everywhere"
+    assert np.all(np.isneginf(lse.cpu().numpy()))
+    assert np.all(k2q_num.cpu().numpy() == 0)
+
+
 def test_deterministic():
     import torch
 
