@@ -356,6 +356,50 @@ def test_split_lists_on_many_streams(oracle_mod):
         compare(bits_from_dev(out), ref, label=f"stream {n % len(streams)}")
 
 
+def test_graph_capture_replays_match_eager(oracle_mod):
+    """After a first call on a stream (which makes that stream's workspace), the
+    layout and the forward can be captured into a HIP graph.  The ragged workload
+    splits lists, so the replays also use the workspace counters, which every launch
+    leaves at zero.  Each replay, with eager work and a sync between, gives the eager
+    result bit for bit."""
+    import torch
+
+    w = gen.ragged(gate=True)
+    tok = [to_dev(w.tok[x]) for x in ("q", "k", "v", "gate")]
+    src = to_dev(w.tile_src_token)
+    idx, num, vbs = to_dev(w.q2k_idx), to_dev(w.q2k_num), to_dev(w.vbs)
+    tiled = [torch.empty((w.B, w.H, w.S, w.D), dtype=torch.bfloat16, device="cuda") for _ in tok]
+    out = torch.empty((w.B, w.H, w.S, w.D), dtype=torch.bfloat16, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+
+    def step():
+        bsa.tile_layout(tok, src, w.T, outs=tiled)
+        bsa.fwd(tiled[0], tiled[1], tiled[2], idx, num, vbs, w.T, out=out)
+
+    with torch.cuda.stream(side):
+        step()  # first call on this stream: its workspace is made here, outside the capture
+    torch.cuda.synchronize()
+    eager = bits_from_dev(out)
+    compare(eager, oracle_out(oracle_mod, w), label="eager ragged")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        step()
+    for r in range(4):
+        out.fill_(float("nan"))
+        for t in tiled:
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits_from_dev(out), eager, err_msg=f"replay {r}")
+        # eager launches between replays share the stream's workspace
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits_from_dev(out), eager, err_msg=f"eager after replay {r}")
+
+
 @pytest.mark.parametrize("D", [64, 128])
 def test_tile_256_random_lists(oracle_mod, D):
     """256-row tiles: lengths above and below 128 (one or two non-empty halves), an
