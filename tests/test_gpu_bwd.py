@@ -16,7 +16,7 @@ import pytest
 
 import block_sparse_tiled_amd as bsa
 from block_sparse_tiled_amd import inputs as gen
-from parity import bits_from_dev, compare_grad, to_dev
+from parity import bits_from_dev, compare_grad, grad_zero_rows, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -82,9 +82,10 @@ def check_problem(w, seed, label, max_k=None):
                 n = min(len(lst), got["k2q_idx"].shape[3])
                 assert got["k2q_idx"][b, h, j, :n].tolist() == lst[:n]
     dq, dk, dv = oracle.bwd(w.q, w.k, w.v, dout, w.q2k_idx, w.q2k_num, w.vbs, w.T)
-    compare_grad(got["dq"], dq, f"{label} dq")
-    compare_grad(got["dk"], dk, f"{label} dk")
-    compare_grad(got["dv"], dv, f"{label} dv")
+    dq_zero, dkv_zero = grad_zero_rows(w.q2k_idx, w.q2k_num, w.vbs, w.T)
+    compare_grad(got["dq"], dq, f"{label} dq", dq_zero)
+    compare_grad(got["dk"], dk, f"{label} dk", dkv_zero)
+    compare_grad(got["dv"], dv, f"{label} dv", dkv_zero)
 
 
 @pytest.mark.parametrize("T,D", [(64, 64), (64, 128), (128, 64), (128, 128), (256, 64), (256, 128)])
@@ -235,5 +236,6 @@ def test_full_size_config(name, heads):
     for b, h in pairs:
         s = _head_slice(w, b, h)
         ref = oracle.bwd(s.q, s.k, s.v, dout[b:b + 1, h:h + 1], s.q2k_idx, s.q2k_num, s.vbs, s.T)
-        for key, r in zip(("dq", "dk", "dv"), ref):
-            compare_grad(got[key][b:b + 1, h:h + 1], r, f"{name} b{b} h{h} {key}")
+        dq_zero, dkv_zero = grad_zero_rows(s.q2k_idx, s.q2k_num, s.vbs, s.T)
+        for key, r, z in zip(("dq", "dk", "dv"), ref, (dq_zero, dkv_zero, dkv_zero)):
+            compare_grad(got[key][b:b + 1, h:h + 1], r, f"{name} b{b} h{h} {key}", z)

@@ -174,3 +174,31 @@ def test_all_minus_inf_row_has_nan_gradients():
     assert np.isneginf(lse[0, 0, 5])  # log of a sum of zeros
     others = np.setdiff1d(np.arange(2 * T), [5])
     assert np.isfinite(out[0, 0, others]).all() and np.isfinite(dq[0, 0, others]).all()
+
+
+def test_structural_zero_rows_of_the_gradients():
+    """The rows the GPU tests require to be +0 bit for bit (padding rows, rows with
+    no key, key tiles nobody lists) are exactly 0 in the oracle; a query row whose
+    only key is a one-row tile has dq = 0 by cancellation (P = 1, dS = dP - D = 0)
+    although it is not such a row."""
+    import sys, os
+
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from parity import grad_zero_rows
+
+    rng = np.random.default_rng(13)
+    for seed, T, vbs in ((21, 64, [64, 1, 0, 37, 64]), (22, 128, [128, 5, 128, 1]), (23, 64, [0, 64, 1])):
+        w = gen.random_problem(seed, B=2, H=2, D=64, T=T, vbs=vbs, density=0.4)
+        dout = rand_dout(rng, w.q.shape)
+        dq, dk, dv = oracle.bwd(w.q, w.k, w.v, dout, w.q2k_idx, w.q2k_num, w.vbs, T)
+        zq, zkv = grad_zero_rows(w.q2k_idx, w.q2k_num, w.vbs, T)
+        assert zq.any() and (~zq).any() and zkv.any() and (~zkv).any()
+        assert not dq[zq].any() and not dk[zkv].any() and not dv[zkv].any()
+        assert np.all(np.abs(dv[~zkv]).sum(-1) > 0)  # every other key row gets dO weight
+    # the cancellation case: query tile 0 lists only the one-row tile 1
+    w = gen.random_problem(24, B=1, H=1, D=64, T=64, vbs=[64, 1], counts=1, MS=1)
+    w.q2k_idx[0, 0, 0, 0] = 1
+    dq, dk, dv = oracle.bwd(w.q, w.k, w.v, rand_dout(rng, w.q.shape), w.q2k_idx, w.q2k_num, w.vbs, 64)
+    zq, _ = grad_zero_rows(w.q2k_idx, w.q2k_num, w.vbs, 64)
+    assert not zq[0, 0, :64].any()
+    assert np.abs(dq[0, 0, :64]).max() < 1e-12
