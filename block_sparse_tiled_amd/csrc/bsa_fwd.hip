@@ -10,7 +10,7 @@
 //  - Attn-QAT commit: full key tiles run without bounds masks; here only
 //    tiles shorter than T take the mask, and only on the 32-key blocks that
 //    reach the valid length.
-// That commit also skips key steps wholly past the valid keys; this kernel
+// That commit also drops key steps entirely beyond the valid keys; this kernel
 // instead runs every tile at full size (masked logits give p = 0 against
 // zeroed V rows, adding exact zeros), which keeps one register assignment
 // for the accumulators across the tile loop.

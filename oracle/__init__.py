@@ -7,8 +7,8 @@ shares no code with it and never falls back to it.
 The functions here follow the FastVideo fastvideo-kernel commit list (page 3):
 
 * ``fwd`` / ``fwd_rows`` -- block-sparse softmax attention, the plain
-  definition written out in ``bsa_oracle.c`` (binary32, as the pages' kernel
-  tests use an FP32 reference; see the 128-token sm_121a forward commit for the
+  definition written out in ``bsa_oracle.c`` (binary32, the precision the pages'
+  kernel tests compare against; see the 128-token sm_121a forward commit for the
   binding's arguments and the hardening commit for the zero-row, NaN-sum and
   padding-key rules).
 * ``tile_layout`` -- the fused layout commit's scatter of token-major Q, K, V

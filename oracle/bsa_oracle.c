@@ -23,8 +23,8 @@
  *       happens only when l != 0 (so a NaN softmax sum yields a NaN row).
  *
  * This is the plain definition of softmax attention restricted to a block
- * mask: no tiling, no online rescaling, no reduced precision for P.  The pages
- * test the kernel against an FP32 reference, so every floating-point step is
+ * mask: no tiling, no online rescaling, no reduced precision for P.  The pages'
+ * kernel tests compare against binary32 results, so every floating-point step is
  * IEEE binary32 with contraction off, in the order written above (dot
  * products over d ascending, sums over keys in list order).  The softmax
  * scale, which the binding does not take as an argument, is 1/sqrt(D)
