@@ -1,7 +1,7 @@
 // Block-sparse tiled attention backward for gfx950 (AMD Instinct MI355X).
 //
 // FastVideo fastvideo-kernel commit list, page 3: the 128-token sm_121a
-// forward commit keeps its binding inference-only because another route's
+// forward commit keeps its binding to the forward because another route's
 // log-sum-exp output feeds an autograd path; the Attn-QAT commit describes a
 // backward of 64x128 dQ and dK/dV tiles.  The pages print no backward
 // formulas; these kernels compute the gradients of the plain forward

@@ -2,7 +2,7 @@
 //
 // FastVideo fastvideo-kernel commit list, page 3:
 //  - 128-token sm_121a forward commit: the operation, (q, k, v, q2k_idx,
-//    q2k_num, variable_block_sizes) -> out, inference only, no log-sum-exp;
+//    q2k_num, variable_block_sizes) -> out, a forward without log-sum-exp;
 //  - hardening commit: a NaN softmax sum yields a NaN row (test l != 0, not
 //    l > 0), rows without keys stay zero, and NaN/Inf in padding rows never
 //    reach the output; its QK/PV overlap (one tile's loads in flight while

@@ -12,7 +12,7 @@ The functions here follow the FastVideo fastvideo-kernel commit list (page 3):
   binding's arguments and the hardening commit for the zero-row, NaN-sum and
   padding-key rules).
 * ``tile_layout`` -- the fused layout commit's scatter of token-major Q, K, V
-  and the gate into the tile buffer in B*H*S*D order, written as the gather it
+  and the gate to their tile rows in B*H*S*D order, written as the gather it
   is equivalent to: output row t of head h reads token ``tile_src_token[t]`` of
   that head, and a row whose source is -1 is padding and holds +0.
 * ``tile_unlayout`` -- the way back from the tile buffer to token-major order

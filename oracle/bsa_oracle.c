@@ -9,7 +9,7 @@
  * What it computes (FastVideo fastvideo-kernel commit list, page 3: the
  * 128-token sm_121a forward commit, which gives the binding
  * block_sparse_sm121_blk128_fwd(q, k, v, q2k_idx, q2k_num, variable_block_sizes)
- * -> {out}, inference only, no LSE; and the hardening commit's kernel bullets
+ * -> {out}, a forward without log-sum-exp; and the hardening commit's kernel bullets
  * on the softmax-sum rule, empty selections and padding keys):
  *
  *   For batch b, head h, query tile i and row r of that tile

@@ -1,6 +1,6 @@
 """Video-latent cube tiling and the inverse layout map (host side, no GPU).
 
-The pages name the scatter of Q, K, V and the gate into a tile buffer
+The pages name the scatter that moves Q, K, V and gate tokens to tile rows
 (FastVideo fastvideo-kernel commit list, page 3, fused-layout commit) but not
 the cube shape or the order inside a cube; both readings are stated in the
 oracle's docstring.  The oracle's map is pinned here to a hand-worked example
