@@ -103,6 +103,9 @@ CASES = {
     # lists longer than one workgroup's list chunk (256 or 128 entries), with
     # repeats and entries naming an empty tile
     "long_lists": (1, 1, lambda T: [T] * 5 + [T - 3, 0], dict(counts=300, MS=300, duplicates=True)),
+    # index rows far wider than the lists they hold: list segments past the
+    # count are empty when the last round is split
+    "wide_rows": (1, 2, lambda T: [T] * 6 + [T - 9], dict(density=0.3, MS=1000)),
 }
 
 
