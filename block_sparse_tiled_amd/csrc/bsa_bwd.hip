@@ -47,10 +47,12 @@ using namespace bsa::detail;
 // ---- transposed lists ---------------------------------------------------------------------
 // One wave per (head, key tile j) scans the head's lists in order (ascending
 // query tile, then list position) and appends i for every live entry equal
-// to j through a ballot-ordered prefix.  Lists of 64 or more positions are
-// read row by row (the count read once per row, 64 contiguous entries per
-// load); shorter ones as one flat range of [NT][MS] entries with four loads
-// in flight, so that a wave does not wait once per short row.
+// to j through a ballot-ordered prefix.  The scan is bound by load latency,
+// so lists of up to 256 positions are read as one flat range of [NT][MS]
+// entries, eight 64-entry loads (and their rows' counts) issued at a time
+// before any of them is used.  Wider lists, whose counts may be far below
+// their width, are read row by row (the count read once per row, only the
+// positions below it loaded).
 __device__ __forceinline__ void k2q_append(bool hit, int value, int& count, int32_t* dst, int max_k,
                                            int lane) {
   const uint64_t m = __ballot(hit);
@@ -69,7 +71,7 @@ __global__ __launch_bounds__(256) void k2q_kernel(const int32_t* __restrict__ q2
                                                   int num_tiles, int max_sel, int64_t n_lists,
                                                   int32_t* __restrict__ k2q_idx,
                                                   int32_t* __restrict__ k2q_num, int max_k) {
-  constexpr int kU = 4;
+  constexpr int kU = 8;
   const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (wid >= n_lists) return;  // whole waves leave together
@@ -80,7 +82,7 @@ __global__ __launch_bounds__(256) void k2q_kernel(const int32_t* __restrict__ q2
   const int32_t* num_h = q2k_num + bh * num_tiles;
   int32_t* dst = k2q_idx + wid * max_k;
   int count = 0;
-  if (max_sel >= 64 || entries + 64 * kU >= (int64_t{1} << 31)) {
+  if (max_sel > 256 || entries + 64 * kU >= (int64_t{1} << 31)) {
     for (int i = 0; i < num_tiles; ++i) {
       const int n = clampi(num_h[i], 0, max_sel);
       for (int base = 0; base < n; base += 64) {
@@ -91,21 +93,26 @@ __global__ __launch_bounds__(256) void k2q_kernel(const int32_t* __restrict__ q2
     }
   } else {
     const uint32_t ms = static_cast<uint32_t>(max_sel);  // entries < 2^31 here
+    const uint32_t last = static_cast<uint32_t>(entries - 1);
     for (uint32_t base = 0; base < entries; base += 64 * kU) {
-      bool hit[kU];
-      int row[kU];
+      // every load first, at positions clamped into the head's range, so that
+      // they are in flight together; positions past the range never hit
+      int x[kU], n[kU], row[kU], e[kU];
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const uint32_t pos = base + 64 * u + lane;
-        row[u] = static_cast<int>(pos / ms);
-        hit[u] = false;
-        if (pos < entries) {
-          const int e = static_cast<int>(pos - row[u] * ms);
-          hit[u] = e < clampi(num_h[row[u]], 0, max_sel) && idx_h[pos] == j;
-        }
+        const uint32_t pc = pos < entries ? pos : last;
+        row[u] = static_cast<int>(pc / ms);
+        e[u] = static_cast<int>(pc - row[u] * ms);
+        x[u] = idx_h[pc];
+        n[u] = num_h[row[u]];
       }
 #pragma unroll
-      for (int u = 0; u < kU; ++u) k2q_append(hit[u], row[u], count, dst, max_k, lane);
+      for (int u = 0; u < kU; ++u) {
+        const bool hit =
+            base + 64 * u + lane < entries && e[u] < clampi(n[u], 0, max_sel) && x[u] == j;
+        k2q_append(hit, row[u], count, dst, max_k, lane);
+      }
     }
   }
   if (lane == 0) k2q_num[wid] = count;  // the true count (the list holds the first max_k)
