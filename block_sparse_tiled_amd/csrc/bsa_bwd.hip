@@ -477,26 +477,36 @@ void dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
           acck[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rb[sl], sb[cc], acck[db], 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
+        // P and dS of this block, four queries (one register group) at a time:
+        // groups 0 and 1 (the first 16-query chunk) once S and dP are complete,
+        // groups 2 and 3 under the MFMAs of the first two dV/dK steps, which
+        // only use the first chunk.
+        // register r holds query 32*qb + 8*(r/4) + 4*half + r%4
+        auto softmax_group = [&](int g) {
+          const float4 l4 = *reinterpret_cast<const float4*>(lse_s + 32 * qb + 8 * g + 4 * half);
+          const float4 d4 = *reinterpret_cast<const float4*>(dlt_s + 32 * qb + 8 * g + 4 * half);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lv[e]));
+            s[r] = pr;                      // P
+            dp[r] = pr * (dp[r] - dv4[e]);  // dS
+          }
+        };
         if (k == NA - 1) {
-          // register r holds query 32*qb + 8*(r/4) + 4*half + r%4: statistics four at a time
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const float4 l4 = *reinterpret_cast<const float4*>(lse_s + 32 * qb + 8 * g + 4 * half);
-            const float4 d4 = *reinterpret_cast<const float4*>(dlt_s + 32 * qb + 8 * g + 4 * half);
-            const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * g + e;
-              const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lv[e]));
-              s[r] = pr;                      // P
-              dp[r] = pr * (dp[r] - dv4[e]);  // dS
-            }
-          }
-#pragma unroll
-          for (int cc = 0; cc < 2; ++cc) {
-            pb[cc] = pack8(s, 8 * cc);
-            sb[cc] = pack8(dp, 8 * cc);
-          }
+          softmax_group(0);
+          softmax_group(1);
+          pb[0] = pack8(s, 0);
+          sb[0] = pack8(dp, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        } else if (k == NA) {
+          softmax_group(2);
+          __builtin_amdgcn_sched_barrier(0);
+        } else if (k == NA + 1) {
+          softmax_group(3);
+          pb[1] = pack8(s, 8);
+          sb[1] = pack8(dp, 8);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
