@@ -25,6 +25,8 @@
 //     per query tile of its transposed list, in blocks of 32 queries: S =
 //     Q K^T, P, dP = dO V^T, dS, then dV^T += dO^T P and dK^T += Q^T dS (dO^T
 //     and Q^T through the LDS transpose read).  K and V stay in registers.
+//     The next block's S and dP products are interleaved with the current
+//     block's dV/dK products, so that the softmax work runs beside MFMAs.
 //   The C-layout-to-B-operand reuse and the key (query) order within a
 //   16-wide chunk are those of the forward (bsa_fwd_common.h).
 //
@@ -36,6 +38,9 @@
 // A row whose softmax sum is NaN (lse NaN, or -inf with keys present)
 // propagates NaN, as the plain formula does.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
+#include <utility>
 
 #include "bsa_fwd_common.h"
 #include "bsa_launch.h"
@@ -334,6 +339,78 @@ void dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 }
 
 // ---- dK, dV -------------------------------------------------------------------------------
+// Issue order of the dK/dV steps of one query tile.  Step qb*(NA+NB) + k is
+// step k of 32-query block qb: S/dP steps (k < NA), then dV/dK steps.  Once
+// a block's P and dS are complete (after its second dV/dK step) its S and dP
+// registers are free, so the next block's S/dP steps are interleaved with
+// the block's remaining dV/dK steps, the last two of which come after them:
+// the next block's softmax then runs beside those two steps' MFMAs.
+template <int NQB, int NA, int NB>
+struct DkvOrder;
+template <int NQB, int NA, int NB>
+inline constexpr DkvOrder<NQB, NA, NB> kDkvOrder{};
+// Calls f(std::integral_constant<int, P>) for P = 0 .. N-1, in order.
+template <typename F, int... P>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, P...>) {
+  (f(std::integral_constant<int, P>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+template <int NQB, int NA, int NB>
+struct DkvOrder {
+  int st[NQB * (NA + NB)];
+  constexpr DkvOrder() : st{} {
+    const int tail = NB - 2 < 2 ? NB - 2 : 2;  // dV/dK steps after the next block's S/dP
+    const int mid = NB - 2 - tail;             // dV/dK steps spread among them
+    int p = 0;
+    for (int a = 0; a < NA; ++a) st[p++] = a;
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int base = qb * (NA + NB), next = base + NA + NB;
+      st[p++] = base + NA;
+      st[p++] = base + NA + 1;
+      int b = 2;
+      if (qb + 1 < NQB) {
+        int a = 0;
+        for (int m = 0; m < mid; ++m) {
+          st[p++] = base + NA + b++;
+          for (int x = mid ? (m + 1) * NA / mid - m * NA / mid : 0; x > 0; --x) st[p++] = next + a++;
+        }
+        while (a < NA) st[p++] = next + a++;
+      }
+      while (b < NB) st[p++] = base + NA + b++;
+    }
+  }
+};
+// An order is valid when it is a permutation of the steps that keeps each
+// block's own steps in order, starts the next block's S/dP after this
+// block's second dV/dK step (the last reader of S and dP), and its dV/dK
+// after all of this block's (the readers of P and dS).
+template <int NQB, int NA, int NB>
+constexpr bool dkv_order_valid() {
+  constexpr int NS = NA + NB, N = NQB * NS;
+  int pos[N] = {};
+  bool seen[N] = {};
+  for (int p = 0; p < N; ++p) {
+    const int st = kDkvOrder<NQB, NA, NB>.st[p];
+    if (st < 0 || st >= N || seen[st]) return false;
+    seen[st] = true;
+    pos[st] = p;
+  }
+  for (int qb = 0; qb < NQB; ++qb) {
+    const int b = qb * NS;
+    for (int k = 1; k < NS; ++k)
+      if (pos[b + k] < pos[b + k - 1]) return false;
+    if (qb + 1 < NQB && (pos[b + NS] < pos[b + NA + 1] || pos[b + NS + NA] < pos[b + NS - 1]))
+      return false;
+  }
+  return true;
+}
+static_assert(dkv_order_valid<4, 8, 8>() && dkv_order_valid<4, 4, 4>() &&
+                  dkv_order_valid<2, 8, 8>() && dkv_order_valid<2, 4, 4>(),
+              "dK/dV step order");
+
 // At D = 128 a wave holds its K and V operands (64 registers) and two fp32
 // accumulators (128) across the whole list: one wave per SIMD, up to 512
 // registers, instead of spilling at two.
@@ -441,7 +518,7 @@ void dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       if (t + 1 < total) issue(t + 1, buf ^ 1);
     // Per 32-query block: S = Q K^T and dP = dO V^T (steps k < NA), P and dS,
     // then dV^T += dO^T P and dK^T += Q^T dS over its two 16-query chunks
-    // (steps k >= NA).  With one wave per SIMD nothing hides LDS latency but
+    // (steps k >= NA), issued in the order kDkvOrder gives.  With one wave per SIMD nothing hides LDS latency but
     // the wave's own MFMAs, so the two LDS operands of every step are read
     // kAhead steps early, through a ring of registers, across blocks and
     // phases.  A wave whose key rows are all padding skips the compute.
@@ -449,8 +526,8 @@ void dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       constexpr int NQB = T / 32, NA = C::kKSteps, NS = NA + 2 * NDB, kSteps = NQB * NS;
       constexpr int kAhead = 3, kRing = kAhead + 1;
       bf16x8_t ra[kRing], rb[kRing];
-      auto load = [&](int st) {
-        const int qb = st / NS, k = st % NS, sl = st % kRing;
+      auto load = [&](int st, int sl) {
+        const int qb = st / NS, k = st % NS;
         if (k < NA) {
           ra[sl] = read_rows<D>(qs, 32 * qb, k, col, half);
           rb[sl] = read_rows<D>(ds_, 32 * qb, k, col, half);
@@ -460,14 +537,42 @@ void dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
           rb[sl] = read_rows_t<D>(qs, 2 * qb + cc, db, lane);
         }
       };
-#pragma unroll
-      for (int st = 0; st < kAhead; ++st) load(st);
+      static_for<kAhead>([&](auto pc) {
+        constexpr int p = decltype(pc)::value;
+        load(kDkvOrder<NQB, NA, 2 * NDB>.st[p], p % kRing);
+      });
       f32x16_t s = zero16, dp = zero16;
       bf16x8_t pb[2], sb[2];
+      // P and dS of block qb, four queries (one register group) at a time:
+      // register r holds query 32*qb + 8*(r/4) + 4*half + r%4
+      auto softmax_group = [&](int qb, int g) {
+        const float4 l4 = *reinterpret_cast<const float4*>(lse_s + 32 * qb + 8 * g + 4 * half);
+        const float4 d4 = *reinterpret_cast<const float4*>(dlt_s + 32 * qb + 8 * g + 4 * half);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-      for (int st = 0; st < kSteps; ++st) {
-        if (st + kAhead < kSteps) load(st + kAhead);
-        const int qb = st / NS, k = st % NS, sl = st % kRing;
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lv[e]));
+          s[r] = pr;                      // P
+          dp[r] = pr * (dp[r] - dv4[e]);  // dS
+        }
+      };
+      static_for<kSteps>([&](auto pc) {
+        constexpr int p = decltype(pc)::value;
+        if constexpr (p + kAhead < kSteps)
+          load(kDkvOrder<NQB, NA, 2 * NDB>.st[p + kAhead], (p + kAhead) % kRing);
+        constexpr int st = kDkvOrder<NQB, NA, 2 * NDB>.st[p];
+        constexpr int qb = st / NS, k = st % NS, sl = p % kRing;
+        if (k == NA) {
+          // the first 16-query chunk, which the first dV/dK steps use, once S
+          // and dP are complete (the MFMAs issued since their last step run
+          // beside it)
+          softmax_group(qb, 0);
+          softmax_group(qb, 1);
+          pb[0] = pack8(s, 0);
+          sb[0] = pack8(dp, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
         if (k < NA) {
           s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[sl], kop[k], k ? s : zero16, 0, 0, 0);
           dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rb[sl], vop[k], k ? dp : zero16, 0, 0, 0);
@@ -477,39 +582,17 @@ void dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
           acck[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rb[sl], sb[cc], acck[db], 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
-        // P and dS of this block, four queries (one register group) at a time:
-        // groups 0 and 1 (the first 16-query chunk) once S and dP are complete,
-        // groups 2 and 3 under the MFMAs of the first two dV/dK steps, which
-        // only use the first chunk.
-        // register r holds query 32*qb + 8*(r/4) + 4*half + r%4
-        auto softmax_group = [&](int g) {
-          const float4 l4 = *reinterpret_cast<const float4*>(lse_s + 32 * qb + 8 * g + 4 * half);
-          const float4 d4 = *reinterpret_cast<const float4*>(dlt_s + 32 * qb + 8 * g + 4 * half);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lv[e]));
-            s[r] = pr;                      // P
-            dp[r] = pr * (dp[r] - dv4[e]);  // dS
-          }
-        };
-        if (k == NA - 1) {
-          softmax_group(0);
-          softmax_group(1);
-          pb[0] = pack8(s, 0);
-          sb[0] = pack8(dp, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        } else if (k == NA) {
-          softmax_group(2);
+        // the second chunk under the MFMAs of the first two dV/dK steps
+        if (k == NA) {
+          softmax_group(qb, 2);
           __builtin_amdgcn_sched_barrier(0);
         } else if (k == NA + 1) {
-          softmax_group(3);
+          softmax_group(qb, 3);
           pb[1] = pack8(s, 8);
           sb[1] = pack8(dp, 8);
           __builtin_amdgcn_sched_barrier(0);
         }
-      }
+      });
     }
   }
   }
