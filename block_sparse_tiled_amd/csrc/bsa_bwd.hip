@@ -222,6 +222,49 @@ __device__ __forceinline__ int item_of(int L, int n_padded) {
   return (L & 7) * (n_padded >> 3) + (L >> 3);
 }
 
+// Instructions [kLo, kHi) of a dma_tile copy of the first `rows` rows of a
+// T x D tile (every one issued; lanes past `rows` fail the range check and
+// read nothing), and the zeroing of padding-row slots those instructions
+// filled: instruction it of a wave fills 1 KiB block it*kWaves + wave, so a
+// contiguous range of instructions covers a contiguous range of rows.
+template <int T, int D, int kLo, int kHi>
+__device__ __forceinline__ void dma_tile_part(const uint16_t* __restrict__ src, uint16_t* lds, int wave,
+                                              const DmaLane<T, D, false>& dl, int rows) {
+  using C = Cfg<T, D>;
+  using DL = DmaLane<T, D, false>;
+  const uint32_t base = launder_s(__builtin_amdgcn_readfirstlane(lds_address(lds)) + wave * 1024);
+  const uint64_t g = reinterpret_cast<uintptr_t>(src);
+  const i32x4_t srd = {static_cast<int>(static_cast<uint32_t>(g)),
+                       static_cast<int>(static_cast<uint32_t>(g >> 32)), rows * D * 2, 0x00020000};
+#pragma unroll
+  for (int it = kLo; it < kHi; ++it) {
+    const uint32_t soff = it * C::kWaves * 1024;
+    dma16(srd, dl.off[it % DL::kN], soff, base + soff);
+  }
+}
+template <int T, int D, int kLo, int kHi>
+__device__ __forceinline__ void zero_padding_part(uint16_t* lds, int vk, int wave, int lane) {
+  using C = Cfg<T, D>;
+  constexpr int kRowsPerBlock = 64 / C::kChunks;
+  const int lane_row = launder(lane) / C::kChunks;
+  uint4* slot = reinterpret_cast<uint4*>(lds) + lane;
+#pragma unroll
+  for (int it = kLo; it < kHi; ++it) {
+    const int blk = it * C::kWaves + wave;
+    if (vk < (blk + 1) * kRowsPerBlock && lane_row >= vk - blk * kRowsPerBlock)  // uniform test first
+      slot[blk * 64] = make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+// Calls f(std::integral_constant<int, P>) for P = 0 .. N-1, in order.
+template <typename F, int... P>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, P...>) {
+  (f(std::integral_constant<int, P>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 // ---- dQ -----------------------------------------------------------------------------------
 template <int T, int D>
 __global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(2, T == 128 ? 2 : 4)))
@@ -282,22 +325,45 @@ void dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const int total = compact_list<T, C::kWaves>(list, base, count, vbs, nt_list, tl, wave_count,
                                                  tid, wave, lane, sub_shift);
     if (total > 0) any_keys = true;
+    // K and V are copied in 64-key halves, each as soon as its LDS half is
+    // free: the next tile's half h once every wave is done with this tile's
+    // half h, so that each half lands while the other half is computed.
+    // Every copy issues all its instructions (padding rows cost no memory
+    // traffic), which keeps the vmcnt waits exact.
+    constexpr int NH = T / 64;                // 64-key halves
+    constexpr int kHP = C::kDmaPerTile / NH;  // copy instructions per half and tensor
+    auto copy_half = [&](auto hc, int j, int vk) {
+      constexpr int h = decltype(hc)::value;
+      dma_tile_part<T, D, h * kHP, (h + 1) * kHP>(kh + static_cast<int64_t>(j) * T * D, ks, wave, dl, vk);
+      dma_tile_part<T, D, h * kHP, (h + 1) * kHP>(vh + static_cast<int64_t>(j) * T * D, vs, wave, dl, vk);
+    };
     for (int t = 0; t < total; ++t) {
       const int2 e = tl[t];
       const int j = __builtin_amdgcn_readfirstlane(e.x);
       const int vk = __builtin_amdgcn_readfirstlane(e.y);
-      wait_vmcnt<0>();  // the operands loaded above
-      dma_tile<T, D, false, true>(kh + static_cast<int64_t>(j) * T * D, ks, wave, dl, vk);
-      dma_tile<T, D, false, true>(vh + static_cast<int64_t>(j) * T * D, vs, wave, dl, vk);
-      wait_vmcnt<0>();
-      if (vk < T) {
-        zero_padding_rows<T, D>(ks, vk, wave, lane);
-        zero_padding_rows<T, D>(vs, vk, wave, lane);
+      int j2 = -1, vk2 = 0;
+      if (t + 1 < total) {
+        const int2 e2 = tl[t + 1];
+        j2 = __builtin_amdgcn_readfirstlane(e2.x);
+        vk2 = __builtin_amdgcn_readfirstlane(e2.y);
       }
-      lds_barrier();
-#pragma unroll
-      for (int hh = 0; hh < T / 64; ++hh) {  // 64 keys: key blocks 2*hh, 2*hh + 1
-        if (wave * 32 >= vq) break;  // every row of this wave is padding: nothing to compute
+      if (t == 0) {
+        wait_vmcnt<0>();  // the operands loaded above
+        static_for<NH>([&](auto hc) { copy_half(hc, j, vk); });
+      }
+      static_for<NH>([&](auto hc) {  // 64 keys: key blocks 2*hh, 2*hh + 1
+        constexpr int hh = decltype(hc)::value;
+        // half hh of this tile has landed; issued after it: its later halves
+        // and, from hh = 2 on, the next tile's halves 0 .. hh - 2
+        wait_vmcnt<2 * kHP * (NH - 1 - hh + (hh > 1 ? hh - 1 : 0))>();
+        if (vk < T) {
+          zero_padding_part<T, D, hh * kHP, (hh + 1) * kHP>(ks, vk, wave, lane);
+          zero_padding_part<T, D, hh * kHP, (hh + 1) * kHP>(vs, vk, wave, lane);
+        }
+        lds_barrier();  // half hh visible; every wave is done with half hh - 1
+        if constexpr (hh > 0)
+          if (j2 >= 0) copy_half(std::integral_constant<int, hh - 1>{}, j2, vk2);
+        if (wave * 32 < vq) {  // a wave whose rows are all padding computes nothing
         f32x16_t s[2], dp[2];
 #pragma unroll
         for (int kk = 0; kk < C::kKSteps; ++kk)
@@ -329,8 +395,10 @@ void dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 read_rows_t<D>(ks, 4 * hh + cc, db, lane), dsk, acc[db], 0, 0, 0);
         }
-      }
-      lds_barrier();  // every wave is done with K and V before the next copies
+        }
+      });
+      lds_barrier();  // every wave is done with the last half
+      if (j2 >= 0) copy_half(std::integral_constant<int, NH - 1>{}, j2, vk2);
     }
   }
   wait_vmcnt<0>();
@@ -349,15 +417,6 @@ template <int NQB, int NA, int NB>
 struct DkvOrder;
 template <int NQB, int NA, int NB>
 inline constexpr DkvOrder<NQB, NA, NB> kDkvOrder{};
-// Calls f(std::integral_constant<int, P>) for P = 0 .. N-1, in order.
-template <typename F, int... P>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, P...>) {
-  (f(std::integral_constant<int, P>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
 template <int NQB, int NA, int NB>
 struct DkvOrder {
   int st[NQB * (NA + NB)];
