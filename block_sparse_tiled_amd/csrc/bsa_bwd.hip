@@ -20,7 +20,9 @@
 //   - dq_kernel: one workgroup per query tile, T/32 waves of 32 query rows;
 //     per listed key tile, in halves of 64 keys: S^T = K Q^T, P^T, dP^T =
 //     V dO^T, dS^T, then dQ^T += K^T dS^T (the K^T operand through the LDS
-//     transpose read).  Q and dO stay in registers as B operands.
+//     transpose read).  Q and dO stay in registers as B operands.  K and V
+//     are copied in the same 64-key halves, each half of the next tile as
+//     soon as every wave is done with that half of the current one.
 //   - dkv_kernel: one workgroup per key tile, T/32 waves of 32 key rows;
 //     per query tile of its transposed list, in blocks of 32 queries: S =
 //     Q K^T, P, dP = dO V^T, dS, then dV^T += dO^T P and dK^T += Q^T dS (dO^T
