@@ -20,6 +20,16 @@ The functions here follow the FastVideo fastvideo-kernel commit list (page 3):
 * ``fwd64`` / ``bwd`` (module ``bsa_bwd``) -- the same forward in fp64 with
   its log-sum-exp, and its gradients dq, dk, dv (the pages' LSE-requiring
   autograd path; formulas in that module's docstring).
+* ``coarse_pool`` / ``coarse_select`` / ``coarse`` -- the coarse stage that
+  chooses each query tile's key tiles (``q2k_idx``, ``q2k_num``) and gives the
+  coarse output.  The pages name the block-sparse kernel the fine attention
+  but do not define this stage; the definition adopted is Video Sparse
+  Attention's coarse stage, written out in ``bsa_oracle.c``: tiles pooled to
+  the mean of their valid rows, binary32 logits of pooled queries against
+  pooled keys, the top-k key tiles per query tile (ties to the lower index),
+  and softmax attention over the pooled tokens.  Its pins
+  (``tests/test_oracle_coarse_pins.py``) are fp64 library routines, brute
+  force and hand-worked cases, not the pages (parity unpinned by the pages).
 * ``cube_tile_map`` -- the tiling of a video latent into 3D cubes that the
   layout step applies (the pages name the scatter into tiles but not the cube
   shape; the cube is an argument, and the plainest order is taken: cubes
@@ -73,6 +83,10 @@ def _load():
     lib.oracle_bsa_fwd_rows.restype = i32
     lib.oracle_softmax_scale.argtypes = [i64]
     lib.oracle_softmax_scale.restype = ctypes.c_float
+    lib.oracle_coarse_pool.argtypes = [p, p, i64, i64, i64, i64, p]
+    lib.oracle_coarse_pool.restype = i32
+    lib.oracle_coarse_select.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, p, p, p]
+    lib.oracle_coarse_select.restype = i32
     _lib = lib
     return lib
 
@@ -218,3 +232,44 @@ def cube_tile_map(latent, cube):
 
 
 from .bsa_bwd import bwd, fwd64  # noqa: E402,F401
+
+
+def coarse_pool(x, vbs, tile):
+    """float32 [B, H, NT, D]: the mean of each tile's valid rows (rows summed in order in
+    binary32, then divided by the count); 0 for a tile with no valid row."""
+    lib = _load()
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    vbs = np.ascontiguousarray(vbs, dtype=np.int32)
+    B, H, S, D = x.shape
+    if S % tile or vbs.shape != (S // tile,):
+        raise ValueError("x must be [B, H, NT*T, D] and block sizes [NT]")
+    NT = S // tile
+    xm = np.empty((B, H, NT, D), np.float32)
+    rc = lib.oracle_coarse_pool(_ptr(x), _ptr(vbs), B * H, NT, tile, D, _ptr(xm))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the problem: {ERRORS.get(rc, rc)}")
+    return xm
+
+
+def coarse_select(qm, km, vm, vbs, topk, max_sel=None):
+    """From pooled tensors [B, H, NT, D] (float32): (q2k_idx int32 [B, H, NT, max_sel],
+    q2k_num int32 [B, H, NT], oc float32 [B, H, NT, D]).  Unused list entries are -1."""
+    lib = _load()
+    qm, km, vm = (np.ascontiguousarray(a, dtype=np.float32) for a in (qm, km, vm))
+    vbs = np.ascontiguousarray(vbs, dtype=np.int32)
+    B, H, NT, D = qm.shape
+    MS = topk if max_sel is None else max_sel
+    idx = np.empty((B, H, NT, MS), np.int32)
+    num = np.empty((B, H, NT), np.int32)
+    oc = np.empty((B, H, NT, D), np.float32)
+    rc = lib.oracle_coarse_select(_ptr(qm), _ptr(km), _ptr(vm), _ptr(vbs), B * H, NT, D, topk, MS,
+                                  _ptr(idx), _ptr(num), _ptr(oc))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the problem: {ERRORS.get(rc, rc)}")
+    return idx, num, oc
+
+
+def coarse(q, k, v, vbs, tile, topk, max_sel=None):
+    """The whole coarse stage on tiled bf16 q, k, v [B, H, NT*T, D]: (q2k_idx, q2k_num, oc)."""
+    return coarse_select(coarse_pool(q, vbs, tile), coarse_pool(k, vbs, tile),
+                         coarse_pool(v, vbs, tile), vbs, topk, max_sel)

@@ -248,3 +248,145 @@ int oracle_bsa_fwd_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
 
 /* The binary32 softmax scale the oracle uses for head dimension D. */
 float oracle_softmax_scale(int64_t D) { return (float)(1.0 / sqrt((double)D)); }
+
+/*
+ * Coarse stage: tile selection (the q2k_idx lists) and the coarse output.
+ *
+ * The pages call the block-sparse kernel the "fine" attention (hardening
+ * commit: the fine-attention override; fused-layout commit: the gate scattered
+ * with Q, K and V) but never say how a query tile's key tiles are chosen.  The
+ * definition adopted is the coarse stage of Video Sparse Attention (Zhang et
+ * al., 2025), written out plainly:
+ *
+ *   pooling   every tile t with vbs[t] > 0 becomes one token, the mean of its
+ *             valid rows: xm[t][d] = (sum over s < vbs[t], ascending, of
+ *             x[t*T + s][d]) / vbs[t], binary32 sums and one division;
+ *   logits    g[i][j] = sum over d ascending of qm[i][d] * km[j][d], binary32
+ *             products and sums (no fused multiply-add);
+ *   selection for a query tile i with vbs[i] > 0, the candidates are the key
+ *             tiles j with vbs[j] > 0, ranked by g[i][j] descending (a NaN
+ *             logit ranks as -inf, -0 as +0), equal logits by ascending j; the
+ *             first k = min(topk, candidates) are kept and listed in
+ *             q2k_idx[i][0..k) by ascending j, q2k_num[i] = k; the other
+ *             entries are -1.  A query tile with vbs[i] = 0 keeps nothing;
+ *   coarse    oc[i] = sum over candidates j (ascending) of p_j * vm[j] / l,
+ *   output    p_j = exp(scale*g[i][j] - m), m = the largest scale*g[i][j],
+ *             l = sum p_j, divided only when l != 0 (as the fine stage);
+ *             0 for a query tile with vbs[i] = 0 or without candidates.
+ *
+ * Everything is binary32 with contraction off, so the lists are a fixed
+ * function of the inputs.
+ */
+
+/* xm [B*H, NT, D]: the mean of each tile's valid rows (0 for empty tiles). */
+int oracle_coarse_pool(const uint16_t *x, const int32_t *vbs, int64_t BH, int64_t NT,
+                       int64_t T, int64_t D, float *xm) {
+  int64_t bh, t, s, d;
+  if (BH < 0 || NT < 0 || T <= 0 || D <= 0) return ORACLE_ERR_ARG;
+  for (t = 0; t < NT; ++t)
+    if (vbs[t] < 0 || vbs[t] > T) return ORACLE_ERR_LENGTH;
+  for (bh = 0; bh < BH; ++bh)
+    for (t = 0; t < NT; ++t)
+      for (d = 0; d < D; ++d) {
+        float acc = 0.0f;
+        const int64_t n = vbs[t];
+        for (s = 0; s < n; ++s) acc = acc + widen_bf16(x[((bh * NT + t) * T + s) * D + d]);
+        xm[(bh * NT + t) * D + d] = n > 0 ? acc / (float)n : 0.0f;
+      }
+  return ORACLE_OK;
+}
+
+/* Ranking key of a logit: NaN as -inf, -0 as +0. */
+static float rank_key(float g) {
+  if (g != g) return -INFINITY;
+  return g == 0.0f ? 0.0f : g;
+}
+
+typedef struct {
+  float key;
+  int64_t j;
+} ranked_t;
+
+/* Ranked order: larger key first, equal keys by ascending tile index (a total
+ * order, so any sort gives the same sequence). */
+static int rank_cmp(const void *pa, const void *pb) {
+  const ranked_t *a = (const ranked_t *)pa, *b = (const ranked_t *)pb;
+  if (a->key > b->key) return -1;
+  if (a->key < b->key) return 1;
+  return a->j < b->j ? -1 : (a->j > b->j ? 1 : 0);
+}
+
+/*
+ * From the pooled tensors: q2k_idx [B*H, NT, MS], q2k_num [B*H, NT], and the
+ * coarse output oc [B*H, NT, D] (float32).  topk >= 0, MS >= topk.
+ */
+int oracle_coarse_select(const float *qm, const float *km, const float *vm, const int32_t *vbs,
+                         int64_t BH, int64_t NT, int64_t D, int64_t topk, int64_t MS,
+                         int32_t *q2k_idx, int32_t *q2k_num, float *oc) {
+  int64_t bh, i, j, d, n;
+  if (BH < 0 || NT < 0 || D <= 0 || topk < 0 || MS < topk) return ORACLE_ERR_ARG;
+  for (j = 0; j < NT; ++j)
+    if (vbs[j] < 0) return ORACLE_ERR_LENGTH;
+  const size_t nt1 = (size_t)(NT > 0 ? NT : 1);
+  float *g = (float *)malloc(sizeof(float) * nt1);
+  ranked_t *order = (ranked_t *)malloc(sizeof(ranked_t) * nt1);
+  char *keep = (char *)malloc(nt1);
+  float *acc = (float *)malloc(sizeof(float) * (size_t)D);
+  if (!g || !order || !keep || !acc) {
+    free(g);
+    free(order);
+    free(keep);
+    free(acc);
+    return ORACLE_ERR_NOMEM;
+  }
+  const float scale = (float)(1.0 / sqrt((double)D));
+  for (bh = 0; bh < BH; ++bh)
+    for (i = 0; i < NT; ++i) {
+      int32_t *list = q2k_idx + (bh * NT + i) * MS;
+      float *o = oc + (bh * NT + i) * D;
+      for (n = 0; n < MS; ++n) list[n] = -1;
+      for (d = 0; d < D; ++d) o[d] = 0.0f;
+      q2k_num[bh * NT + i] = 0;
+      if (vbs[i] <= 0) continue;
+      /* logits of the candidates, ascending j */
+      int64_t cand = 0;
+      for (j = 0; j < NT; ++j) {
+        keep[j] = 0;
+        if (vbs[j] <= 0) continue;
+        float dot = 0.0f;
+        for (d = 0; d < D; ++d)
+          dot = dot + qm[(bh * NT + i) * D + d] * km[(bh * NT + j) * D + d];
+        g[j] = dot;
+        order[cand].key = rank_key(dot);
+        order[cand].j = j;
+        ++cand;
+      }
+      if (cand == 0) continue;
+      qsort(order, (size_t)cand, sizeof(ranked_t), rank_cmp);
+      const int64_t k = topk < cand ? topk : cand;
+      for (n = 0; n < k; ++n) keep[order[n].j] = 1;
+      int64_t w = 0;
+      for (j = 0; j < NT; ++j)
+        if (vbs[j] > 0 && keep[j]) list[w++] = (int32_t)j;
+      q2k_num[bh * NT + i] = (int32_t)k;
+      /* coarse output over every candidate, ascending j */
+      float mx = -INFINITY;
+      for (j = 0; j < NT; ++j)
+        if (vbs[j] > 0 && scale * g[j] > mx) mx = scale * g[j];
+      float l = 0.0f;
+      for (d = 0; d < D; ++d) acc[d] = 0.0f;
+      for (j = 0; j < NT; ++j) {
+        if (vbs[j] <= 0) continue;
+        const float p = expf(scale * g[j] - mx);
+        l = l + p;
+        for (d = 0; d < D; ++d) acc[d] = acc[d] + p * vm[(bh * NT + j) * D + d];
+      }
+      if (l != 0.0f)
+        for (d = 0; d < D; ++d) o[d] = acc[d] / l;
+    }
+  free(g);
+  free(order);
+  free(keep);
+  free(acc);
+  return ORACLE_OK;
+}
