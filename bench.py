@@ -7,9 +7,10 @@ already resident in HBM: the fused token-to-tile layout of Q, K, V and the gate
 (bsa_fwd, one launch).  The reported value is effective TFLOP/s counting only
 the valid tokens of the selected tiles (4*D*vbs[i]*vbs[j] per listed pair).
 
-Prints one JSON line.  Default workload: the 128-token ragged shape
-(B=1, H=12, D=128, 64 tiles of 128 with lengths U{96..128} and a last tile of
-57, 16 of 64 key tiles per query tile, 38 empty lists).
+Prints one JSON line.  Default workload: the dense-limit shape (B=1, H=6,
+D=128, 31200 tokens in 244 tiles of 128, the last of 96; every query tile
+lists every key tile), the largest configuration and the one the 50 % target
+is set on.  --workload picks another.
 """
 from __future__ import annotations
 
@@ -87,6 +88,17 @@ def run_env(dev):
             "torch": torch.__version__, "hip": torch.version.hip}
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_threads():
     try:
         n = len(os.sched_getaffinity(0))
@@ -98,8 +110,10 @@ def cpu_threads():
     return max(1, n)
 
 
-def cpu_baseline(w, kv, budget_flops):
-    """Time the CPU oracle (as is) on a bounded sample of the workload's rows."""
+def cpu_baseline(w, kv, budget_flops, threads=None, seconds=10.0):
+    """Time the CPU oracle (as is) on a bounded sample of the workload's rows: whole
+    non-empty query tiles in a seeded random order up to ``budget_flops``, repeated
+    until about ``seconds`` of wall time (at most three times that)."""
     import oracle
 
     items = np.argwhere(kv > 0)  # (b, h, i) with keys
@@ -115,10 +129,9 @@ def cpu_baseline(w, kv, budget_flops):
         rows.extend(range(base, base + vq))
         flops += f
     rows = np.array(rows, np.int64)
-    threads = cpu_threads()
-    # repeat the sample until about 10 s of wall time (at most 30 s) so the rate is stable
+    threads = cpu_threads() if threads is None else threads
     passes, dt = 0, 0.0
-    while dt < 10.0 and (passes == 0 or dt * (passes + 1) / passes < 30.0):
+    while dt < seconds and (passes == 0 or dt * (passes + 1) / passes < 3 * seconds):
         t0 = time.perf_counter()
         oracle.fwd_rows(w.q, w.k, w.v, w.q2k_idx, w.q2k_num, w.vbs, w.T, rows, nthreads=threads)
         dt += time.perf_counter() - t0
@@ -130,10 +143,32 @@ def cpu_baseline(w, kv, budget_flops):
         "cores": threads,
         "kind": "oracle",
         "sample": f"{n_items} of {int((kv > 0).sum())} non-empty query tiles ({rows.size} valid "
-                  f"rows, {flops / 1e9:.1f} GFLOP) of the same workload, fp32 C oracle, "
+                  f"rows, {flops / 1e9:.2f} GFLOP) of the same workload, fp32 C oracle, "
                   f"{passes} passes in {dt:.1f} s",
-        "seconds": dt,
+        "seconds": round(dt, 2),
     }
+
+
+def cpu_protocol(bench_name, bench_w, bench_kv):
+    """The oracle timed on every configuration: all host threads on each (a bounded
+    sample, about 3 s), and one thread on the tiny and ragged configurations."""
+    from block_sparse_tiled_amd import inputs as gen
+
+    res = {"all_threads": {}, "single_thread": {}}
+    for name in ("tiny", "ragged", "video", "dense", "stress"):
+        if name == bench_name:
+            w, kv = bench_w, bench_kv
+        else:
+            w = gen.make(name)
+            kv = pair_flops(w)[1]
+        print(f"[bench] CPU oracle on {name}", file=sys.stderr, flush=True)
+        cb = cpu_baseline(w, kv, 8e9, seconds=3.0)
+        res["all_threads"][WORKLOAD_NAMES[name]] = {k: cb[k] for k in ("value", "cores", "sample")}
+        if name in ("tiny", "ragged"):
+            cb1 = cpu_baseline(w, kv, 1e9, threads=1, seconds=3.0)
+            res["single_thread"][WORKLOAD_NAMES[name]] = {k: cb1[k] for k in ("value", "sample")}
+        del w, kv
+    return res
 
 
 def run_backward(args, w, flops_fwd, put, dev):
@@ -150,21 +185,24 @@ def run_backward(args, w, flops_fwd, put, dev):
     from block_sparse_tiled_amd import inputs as gen
 
     dout = put(gen.to_bf16_bits(rng.standard_normal(w.q.shape).astype(np.float32)))
-    out = torch.empty_like(q)
+    out, out_lo = torch.empty_like(q), torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
     stream = torch.cuda.current_stream(dev)
+    ws_bytes = bsa.workspace_size(w.B, w.H, w.NT, w.T, w.D, w.MS)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        bsa.fwd_lse(q, k, v, idx, num, vbs, w.T, out=out, lse=lse)
+        bsa.fwd_lse(q, k, v, idx, num, vbs, w.T, out=out, lse=lse, out_lo=out_lo, workspace=ws)
         if ev is not None:
             ev[1].record(stream)
         k2q_idx, k2q_num = bsa.bwd_k2q(idx, num)
         if ev is not None:
             ev[2].record(stream)
-        bsa.bwd(q, k, v, out, dout, lse, idx, num, k2q_idx, k2q_num, vbs, w.T, dq=dq, dk=dk, dv=dv)
+        bsa.bwd(q, k, v, out, out_lo, dout, lse, idx, num, k2q_idx, k2q_num, vbs, w.T, dq=dq, dk=dk,
+                dv=dv)
         if ev is not None:
             ev[3].record(stream)
 
@@ -214,7 +252,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="ragged", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--workload", default="dense", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-gflop", type=float, default=80.0,
                     help="size of the row sample the CPU oracle is timed on")
@@ -227,7 +265,11 @@ def main():
                     help="also time this many forward calls, each after a 1 GiB scratch write "
                          "(cache-cold; off by default so that profiles count only the timed steps)")
     ap.add_argument("--fwd-only", action="store_true",
-                    help="time only the attention launch (no layout) -- for profiling")
+                    help="time only the attention launch (the tile buffers are laid out once "
+                         "before timing) -- for profiling")
+    ap.add_argument("--cpu-protocol", action=argparse.BooleanOptionalAction, default=True,
+                    help="also time the oracle on every configuration (all threads; one thread "
+                         "on tiny and ragged)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -266,6 +308,10 @@ def main():
     tiled = [torch.empty((w.B, w.H, w.S, w.D), dtype=torch.bfloat16, device=dev) for _ in tok]
     out = torch.empty((w.B, w.H, w.S, w.D), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
+    ws_bytes = bsa.workspace_size(w.B, w.H, w.NT, w.T, w.D, w.MS)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    if args.fwd_only:  # the forward always reads the laid-out inputs, never uninitialised memory
+        bsa.tile_layout(tok, src_map, w.T, outs=tiled)
 
     def step(ev=None):
         if not args.fwd_only:
@@ -274,7 +320,7 @@ def main():
             bsa.tile_layout(tok, src_map, w.T, outs=tiled)
         if ev is not None:
             ev[1].record(stream)
-        bsa.fwd(tiled[0], tiled[1], tiled[2], idx, num, vbs, w.T, out=out)
+        bsa.fwd(tiled[0], tiled[1], tiled[2], idx, num, vbs, w.T, out=out, workspace=ws)
         if ev is not None:
             ev[2].record(stream)
 
@@ -330,7 +376,7 @@ def main():
         for c in range(args.cold):
             scratch.fill_(float(c))
             cold_ev[c][0].record(stream)
-            bsa.fwd(tiled[0], tiled[1], tiled[2], idx, num, vbs, w.T, out=out)
+            bsa.fwd(tiled[0], tiled[1], tiled[2], idx, num, vbs, w.T, out=out, workspace=ws)
             cold_ev[c][1].record(stream)
         torch.cuda.synchronize()
         cold_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in cold_ev]))
@@ -354,8 +400,9 @@ def main():
             "valid_tokens": int(w.vbs.sum()),
             "flops_valid_tokens": flops,
             "flops_full_tiles": full_tile_flops(w),
-            "step": "fwd only" if args.fwd_only else
-                    "bsa_tile_layout(q,k,v,gate) + bsa_fwd, inputs resident in HBM",
+            "step": "bsa_fwd only (tile buffers laid out once before timing)" if args.fwd_only
+                    else "bsa_tile_layout(q,k,v,gate) + bsa_fwd, inputs resident in HBM",
+            "workspace_bytes": ws_bytes,
         },
         "pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_ms": round(fwd_avg, 5),
@@ -397,9 +444,14 @@ def main():
         try:
             cb = cpu_baseline(w, kv, args.cpu_budget_gflop * 1e9)
             cb["value"] = round(cb["value"], 6)
+            cb["cpu_model"] = cpu_model()
+            if args.cpu_protocol:
+                del tok, tiled, out, ws
+                cb["protocol"] = cpu_protocol(args.workload, w, kv)
         except Exception as e:  # the GPU figures stand on their own; say why the baseline is missing
             print(f"[bench] CPU baseline failed: {e!r}", file=sys.stderr, flush=True)
-            cb = {"value": None, "unit": "TFLOP/s", "kind": "oracle", "error": repr(e)}
+            cb = {"value": None, "unit": "TFLOP/s", "kind": "oracle", "error": repr(e),
+                  "cpu_model": cpu_model()}
         rec["cpu_baseline"] = cb
     else:
         rec["cpu_baseline"] = None

@@ -17,4 +17,5 @@ from .api import (  # noqa: F401
     tile_unlayout,
     within_launch_limits,
     within_launch_limits_py,
+    workspace_size,
 )

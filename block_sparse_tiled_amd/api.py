@@ -54,16 +54,19 @@ def load():
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     lib.bsa_within_launch_limits.argtypes = [i64, i64, i64, i64]
     lib.bsa_within_launch_limits.restype = ctypes.c_int
-    lib.bsa_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, i64, i64, i64, i32, i32, vp]
+    lib.bsa_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, i64, i64, i64, i32, i32, vp, i64, vp]
     lib.bsa_fwd.restype = ctypes.c_int
+    lib.bsa_fwd_workspace_size.argtypes = [i64, i64, i64, i32, i32, i32, ctypes.POINTER(i64)]
+    lib.bsa_fwd_workspace_size.restype = ctypes.c_int
     lib.bsa_tile_layout.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp, i32,
                                     i64, i64, i64, i64, i32, vp]
     lib.bsa_tile_layout.restype = ctypes.c_int
-    lib.bsa_fwd_lse.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, i64, i64, i64, i32, i32, vp]
+    lib.bsa_fwd_lse.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, i64, i64, i64, i32, i32,
+                                vp, i64, vp]
     lib.bsa_fwd_lse.restype = ctypes.c_int
     lib.bsa_bwd_k2q.argtypes = [vp, vp, i64, i64, i64, i32, vp, vp, i32, vp]
     lib.bsa_bwd_k2q.restype = ctypes.c_int
-    lib.bsa_bwd.argtypes = [vp] * 11 + [i32] + [vp] * 4 + [i64, i64, i64, i32, i32, i32, vp]
+    lib.bsa_bwd.argtypes = [vp] * 12 + [i32] + [vp] * 4 + [i64, i64, i64, i32, i32, i32, vp]
     lib.bsa_bwd.restype = ctypes.c_int
     lib.bsa_tile_unlayout.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp, i32,
                                       i64, i64, i64, i64, i32, vp]
@@ -134,46 +137,61 @@ def fwd_out_shape(q_shape):
     return tuple(q_shape)
 
 
-def fwd(q, k, v, q2k_idx, q2k_num, block_sizes, tile, out=None):
+def workspace_size(batch, heads, num_tiles, tile, head_dim, max_sel):
+    """Bytes of workspace ``fwd`` and ``fwd_lse`` use for this shape on the current
+    device (0 when the call never cuts tile lists)."""
+    lib = load()
+    n = ctypes.c_int64(0)
+    _check(lib.bsa_fwd_workspace_size(batch, heads, num_tiles, tile, head_dim, max_sel,
+                                      ctypes.byref(n)))
+    return int(n.value)
+
+
+def _workspace(workspace, device, B, H, NT, tile, D, MS):
+    """(pointer, bytes) of the workspace argument: "auto" allocates the size the
+    library asks for (through torch's caching allocator), None passes none (whole
+    query tiles only), a uint8 cuda tensor is used as given."""
+    import torch
+
+    if workspace is None:
+        return None, ctypes.c_void_p(0), 0
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError('workspace must be "auto", None or a uint8 cuda tensor')
+        with torch.cuda.device(device):
+            n = workspace_size(B, H, NT, tile, D, MS)
+        if n == 0:
+            return None, ctypes.c_void_p(0), 0
+        workspace = torch.empty(n, dtype=torch.uint8, device=device)
+    _require(workspace, "workspace", torch.uint8, device, 1)
+    return workspace, _ptr(workspace), workspace.numel()
+
+
+def fwd(q, k, v, q2k_idx, q2k_num, block_sizes, tile, out=None, workspace="auto"):
     """Block-sparse tiled attention forward on the current stream.
 
     q, k, v: bf16 [B, H, NT*tile, D] cuda tensors; q2k_idx int32 [B, H, NT, MS];
     q2k_num int32 [B, H, NT]; block_sizes int32 [NT].  Returns ``out`` (bf16,
-    same shape as q), allocated with ``torch.empty`` when not given.
+    same shape as q), allocated with ``torch.empty`` when not given.  ``workspace``:
+    "auto" (allocate what the library asks for), None (no workspace: whole query
+    tiles only) or a uint8 cuda tensor of at least ``workspace_size`` bytes.
     """
     import torch
 
     lib = load()
-    device = q.device
-    if device.type != "cuda":
-        raise ValueError("bsa.fwd runs on a GPU: q must be a cuda tensor")
-    for t, name in ((q, "q"), (k, "k"), (v, "v")):
-        _require(t, name, torch.bfloat16, device, 4)
-    if k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k and v must have the same shape")
-    B, H, S, D = q.shape
-    if tile not in TILES:
-        raise ValueError(f"tile must be 64, 128 or 256, got {tile}")
-    if S % tile:
-        raise ValueError(f"sequence length {S} is not a multiple of the tile {tile}")
-    NT = S // tile
-    _require(q2k_idx, "q2k_idx", torch.int32, device, 4)
-    _require(q2k_num, "q2k_num", torch.int32, device, 3)
-    _require(block_sizes, "block_sizes", torch.int32, device, 1)
-    if tuple(q2k_idx.shape[:3]) != (B, H, NT) or tuple(q2k_num.shape) != (B, H, NT):
-        raise ValueError("q2k_idx must be [B, H, NT, MS] and q2k_num [B, H, NT]")
-    if tuple(block_sizes.shape) != (NT,):
-        raise ValueError("block_sizes must be [NT]")
+    device, B, H, S, D, NT = _fwd_args(q, k, v, q2k_idx, q2k_num, block_sizes, tile)
     if out is None:
         out = torch.empty_like(q)
     else:
         _require(out, "out", torch.bfloat16, device, 4)
         if out.shape != q.shape:
             raise ValueError("out must have q's shape")
+    MS = int(q2k_idx.shape[3])
+    ws, ws_ptr, ws_bytes = _workspace(workspace, device, B, H, NT, tile, D, MS)
     with torch.cuda.device(device):
         _check(lib.bsa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(q2k_idx), _ptr(q2k_num),
-                           _ptr(block_sizes), tile, _ptr(out), B, H, NT, D,
-                           int(q2k_idx.shape[3]), _stream_handle(device)))
+                           _ptr(block_sizes), tile, _ptr(out), B, H, NT, D, MS, ws_ptr, ws_bytes,
+                           _stream_handle(device)))
     return out
 
 
@@ -316,23 +334,30 @@ def _fwd_args(q, k, v, q2k_idx, q2k_num, block_sizes, tile):
     return device, B, H, S, D, NT
 
 
-def fwd_lse(q, k, v, q2k_idx, q2k_num, block_sizes, tile, out=None, lse=None):
-    """``fwd`` that also returns each row's log-sum-exp (float32 [B, H, NT*tile])."""
+def fwd_lse(q, k, v, q2k_idx, q2k_num, block_sizes, tile, out=None, lse=None, out_lo=None,
+            workspace="auto"):
+    """``fwd`` that also returns the statistics the backward needs: (out, lse, out_lo)
+    with lse float32 [B, H, NT*tile] (each row's log-sum-exp) and out_lo bf16 like out
+    (the rounding residual of out: out + out_lo is the fp32 result)."""
     import torch
 
     lib = load()
     device, B, H, S, D, NT = _fwd_args(q, k, v, q2k_idx, q2k_num, block_sizes, tile)
     out = torch.empty_like(q) if out is None else out
+    out_lo = torch.empty_like(q) if out_lo is None else out_lo
     lse = torch.empty((B, H, S), dtype=torch.float32, device=device) if lse is None else lse
     _require(out, "out", torch.bfloat16, device, 4)
+    _require(out_lo, "out_lo", torch.bfloat16, device, 4)
     _require(lse, "lse", torch.float32, device, 3)
-    if out.shape != q.shape or tuple(lse.shape) != (B, H, S):
-        raise ValueError("out must have q's shape and lse [B, H, S]")
+    if out.shape != q.shape or out_lo.shape != q.shape or tuple(lse.shape) != (B, H, S):
+        raise ValueError("out and out_lo must have q's shape and lse [B, H, S]")
+    MS = int(q2k_idx.shape[3])
+    ws, ws_ptr, ws_bytes = _workspace(workspace, device, B, H, NT, tile, D, MS)
     with torch.cuda.device(device):
         _check(lib.bsa_fwd_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(q2k_idx), _ptr(q2k_num),
-                               _ptr(block_sizes), tile, _ptr(out), _ptr(lse), B, H, NT, D,
-                               int(q2k_idx.shape[3]), _stream_handle(device)))
-    return out, lse
+                               _ptr(block_sizes), tile, _ptr(out), _ptr(out_lo), _ptr(lse), B, H,
+                               NT, D, MS, ws_ptr, ws_bytes, _stream_handle(device)))
+    return out, lse, out_lo
 
 
 def bwd_k2q(q2k_idx, q2k_num, max_k=None):
@@ -355,16 +380,16 @@ def bwd_k2q(q2k_idx, q2k_num, max_k=None):
     return k2q_idx, k2q_num
 
 
-def bwd(q, k, v, out, dout, lse, q2k_idx, q2k_num, k2q_idx, k2q_num, block_sizes, tile,
+def bwd(q, k, v, out, out_lo, dout, lse, q2k_idx, q2k_num, k2q_idx, k2q_num, block_sizes, tile,
         dq=None, dk=None, dv=None):
     """Gradients (dq, dk, dv), bf16 like q, of the block-sparse forward for the upstream
-    gradient ``dout``; ``out`` and ``lse`` come from ``fwd_lse``, the transposed lists
-    from ``bwd_k2q``."""
+    gradient ``dout``; ``out``, ``out_lo`` and ``lse`` come from ``fwd_lse``, the
+    transposed lists from ``bwd_k2q``."""
     import torch
 
     lib = load()
     device, B, H, S, D, NT = _fwd_args(q, k, v, q2k_idx, q2k_num, block_sizes, tile)
-    for t, name in ((out, "out"), (dout, "dout")):
+    for t, name in ((out, "out"), (out_lo, "out_lo"), (dout, "dout")):
         _require(t, name, torch.bfloat16, device, 4)
         if t.shape != q.shape:
             raise ValueError(f"{name} must have q's shape")
@@ -383,7 +408,8 @@ def bwd(q, k, v, out, dout, lse, q2k_idx, q2k_num, k2q_idx, k2q_num, block_sizes
         grads.append(g)
     delta = torch.empty((B, H, S), dtype=torch.float32, device=device)
     with torch.cuda.device(device):
-        _check(lib.bsa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+        _check(lib.bsa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(out_lo), _ptr(dout),
+                           _ptr(lse),
                            _ptr(q2k_idx), _ptr(q2k_num), _ptr(k2q_idx), _ptr(k2q_num),
                            _ptr(block_sizes), tile, _ptr(grads[0]), _ptr(grads[1]),
                            _ptr(grads[2]), _ptr(delta), B, H, NT, D, int(q2k_idx.shape[3]),

@@ -16,7 +16,12 @@
 //     whose lists name it, ascending, a tile listed twice appearing twice),
 //     built deterministically: one wave per key tile scans the lists in
 //     order with a ballot-ordered append.
-//   - delta_kernel: D_r = dO_r . out_r in fp32 (0 for padding rows).
+//   - delta_kernel: D_r = dO_r . o_r in fp32 (0 for padding rows), with o_r
+//     the forward's fp32 result rebuilt as out + out_lo (the stored bf16
+//     output plus its bf16 rounding residual).  On a peaked row dS = P(dP - D)
+//     is a small difference of nearly equal terms, and D from the bf16 out
+//     alone would carry an error of 2^-9 of |dO||o|, which then dominates dq
+//     and dk.
 //   - dq_kernel: one workgroup per query tile, T/32 waves of 32 query rows;
 //     per listed key tile, in halves of 64 keys: S^T = K Q^T, P^T, dP^T =
 //     V dO^T, dS^T, then dQ^T += K^T dS^T (the K^T operand through the LDS
@@ -125,9 +130,10 @@ __global__ __launch_bounds__(256) void k2q_kernel(const int32_t* __restrict__ q2
   if (lane == 0) k2q_num[wid] = count;  // the true count (the list holds the first max_k)
 }
 
-// ---- D = rowsum(dO * out) -----------------------------------------------------------------
+// ---- D = rowsum(dO * (out + out_lo)) ------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void delta_kernel(const uint16_t* __restrict__ out,
+                                                    const uint16_t* __restrict__ out_lo,
                                                     const uint16_t* __restrict__ dout,
                                                     const int32_t* __restrict__ vbs, int num_tiles,
                                                     int tile, int64_t rows,
@@ -145,12 +151,16 @@ __global__ __launch_bounds__(256) void delta_kernel(const uint16_t* __restrict__
     valid = static_cast<int>(r % tile) < vq;
     if (valid) {
       const uint4 o = *reinterpret_cast<const uint4*>(out + row * D + 8 * part);
+      const uint4 ol = *reinterpret_cast<const uint4*>(out_lo + row * D + 8 * part);
       const uint4 g = *reinterpret_cast<const uint4*>(dout + row * D + 8 * part);
-      const uint32_t ow[4] = {o.x, o.y, o.z, o.w}, gw[4] = {g.x, g.y, g.z, g.w};
+      const uint32_t ow[4] = {o.x, o.y, o.z, o.w}, lw[4] = {ol.x, ol.y, ol.z, ol.w};
+      const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        acc += __uint_as_float(ow[x] << 16) * __uint_as_float(gw[x] << 16);
-        acc += __uint_as_float(ow[x] & 0xffff0000u) * __uint_as_float(gw[x] & 0xffff0000u);
+        acc += (__uint_as_float(ow[x] << 16) + __uint_as_float(lw[x] << 16)) *
+               __uint_as_float(gw[x] << 16);
+        acc += (__uint_as_float(ow[x] & 0xffff0000u) + __uint_as_float(lw[x] & 0xffff0000u)) *
+               __uint_as_float(gw[x] & 0xffff0000u);
       }
     }
   }
@@ -701,11 +711,11 @@ hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
   const int64_t blocks = (rows * lanes + 255) / 256;
   if (p.head_dim == 128)
     hipLaunchKernelGGL(delta_kernel<128>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
-                       p.out, p.dout, p.block_sizes, p.num_tiles, p.tile, rows, p.delta,
+                       p.out, p.out_lo, p.dout, p.block_sizes, p.num_tiles, p.tile, rows, p.delta,
                        p.sub_shift);
   else
     hipLaunchKernelGGL(delta_kernel<64>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
-                       p.out, p.dout, p.block_sizes, p.num_tiles, p.tile, rows, p.delta,
+                       p.out, p.out_lo, p.dout, p.block_sizes, p.num_tiles, p.tile, rows, p.delta,
                        p.sub_shift);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;

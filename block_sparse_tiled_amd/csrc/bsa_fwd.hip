@@ -50,10 +50,12 @@
 // are interleaved with the MFMAs of the current one.
 //
 // Split items.  A segment stores its (m, l, unnormalised O) partial in a
-// workspace slot and counts its arrival; the last segment to arrive merges
-// the partials in segment order (the same guarded rescaling as the online
-// update, so the result does not depend on which segment merges) and stores
-// the rows.
+// slot of the caller's workspace; a second, small launch on the same stream
+// merges each split item's partials in segment order (the same guarded
+// rescaling as the online update) and stores its rows.  The kernel boundary
+// orders the partial stores before their reads on every XCD, so the
+// workspace is ordinary device memory and needs no counters, atomics or
+// clearing.
 //
 // The MFMA and LDS-transpose register layouts relied on are listed in
 // bsa_fwd_common.h.
@@ -67,6 +69,8 @@
 //     logits -inf) or l is NaN, acc / l otherwise; padding query rows are 0.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "bsa_fwd_common.h"
 #include "bsa_launch.h"
 
@@ -74,14 +78,6 @@ namespace {
 
 using namespace bsa::detail;
 
-// Partials cross workgroups, and XCDs, through the workspace, which is
-// uncached device memory: plain loads, stores and device-scope atomics on it
-// go to memory and are coherent across the XCDs' separate L2 caches without
-// any cache maintenance.  (A device-scope fence would write back and
-// invalidate the whole L2 of the XCD, and with it the K and V tiles the other
-// workgroups reuse; device-coherent sc1 accesses on cached memory proved as
-// costly.)
-//
 // Partial results of a split item, one slot per segment: the unnormalised
 // accumulator in register order (float index (((wave*kDBlocks + db)*4 + r/4)
 // *64 + lane)*4 + r%4), then per lane the running max and this half-wave's
@@ -96,14 +92,78 @@ struct Slot {
   static constexpr int kFloats = kAny + 64;  // keeps slots 256-byte aligned
 };
 
+// Normalise and store the 32 x D rows of one wave of query tile `itile` of
+// head `ibh` (0 for padding query rows and rows without keys; NaN when l == 0
+// or l is NaN).  acc, m_run and l_run are the wave's accumulators in the
+// kernel's register layout (l_run: this half-wave's share of the sum).  With
+// lse, also each row's log-sum-exp and, in out_lo, the bf16 rounding residual
+// of every stored value (out_lo = bf16(o - out) for the fp32 result o), from
+// which the backward forms dO . o to about 2^-17 of its size.
 template <int T, int D>
+__device__ __forceinline__ void store_tile_rows(const f32x16_t* acc, float m_run, float l_run,
+                                                bool any_keys, int64_t ibh, int itile,
+                                                int num_tiles, const int32_t* __restrict__ vbs,
+                                                int sub_shift, int wave, int lane, float c,
+                                                uint16_t* __restrict__ out, float* __restrict__ lse,
+                                                uint16_t* __restrict__ out_lo) {
+  using C = Cfg<T, D>;
+  const int vq = clampi(vbs[itile >> sub_shift] - T * (itile & ((1 << sub_shift) - 1)), 0, T);
+  const int ln = launder(lane);  // per-lane addresses computed here, not hoisted
+  const int row = wave * 32 + (ln & 31);
+  float l_tot;
+  {
+    float lo_half, hi_half;
+    swap_halves(l_run, lo_half, hi_half);
+    l_tot = lo_half + hi_half;
+  }
+  const bool zero_row = !any_keys || row >= vq;
+  const float inv = l_tot != 0.0f ? 1.0f / l_tot : __builtin_nanf("");
+  const int64_t row_id = (ibh * num_tiles + itile) * T + row;
+  if (lse != nullptr && ln < 32) {
+    // natural-log log-sum-exp of the scaled logits: (m*c + log2 l) * ln 2,
+    // with the exponent offset m*c taken as 0 while m is -inf (then l is 0
+    // and the result -inf); -inf for padding rows and rows without keys
+    const float mc = (m_run == -INFINITY ? 0.0f : m_run) * c;
+    lse[row_id] = zero_row ? -INFINITY : (mc + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+  }
+  const int64_t off = row_id * D + 4 * (ln >> 5);
+#pragma unroll
+  for (int db = 0; db < C::kDBlocks; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = zero_row ? 0.0f : acc[db][4 * g + e] * inv;
+      const unsigned w0 = __builtin_bit_cast(unsigned, to_bf16x2(x[0], x[1]));
+      const unsigned w1 = __builtin_bit_cast(unsigned, to_bf16x2(x[2], x[3]));
+      *reinterpret_cast<uint2*>(out + off + 32 * db + 8 * g) = make_uint2(w0, w1);
+      if (lse != nullptr) {
+        // element 0 of a bf16 pair is its low half
+        const float r0 = x[0] - __uint_as_float(w0 << 16);
+        const float r1 = x[1] - __uint_as_float(w0 & 0xffff0000u);
+        const float r2 = x[2] - __uint_as_float(w1 << 16);
+        const float r3 = x[3] - __uint_as_float(w1 & 0xffff0000u);
+        *reinterpret_cast<uint2*>(out_lo + off + 32 * db + 8 * g) =
+            make_uint2(__builtin_bit_cast(unsigned, to_bf16x2(r0, r1)),
+                       __builtin_bit_cast(unsigned, to_bf16x2(r2, r3)));
+      }
+    }
+}
+
+// kTrain: the forward of the training path (bsa_fwd_lse).  It writes the
+// log-sum-exp and the output's rounding residual, and its exponent offset
+// follows the running max eagerly, so that a row's largest logit gets
+// p = exp2(0) = 1, which bf16 holds exactly: on a sharply peaked row the bf16
+// rounding of that one p would otherwise enter o at 2^-9 of |o| and, through
+// D = dO . o, dominate the backward's dS = P (dP - D).
+template <int T, int D, bool kTrain>
 __global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(2, T == 128 ? 2 : 4)))
 void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                     const uint16_t* __restrict__ v, const int32_t* __restrict__ q2k_idx,
                     const int32_t* __restrict__ q2k_num, const int32_t* __restrict__ vbs,
                     uint16_t* __restrict__ out, int num_tiles, int max_sel, int n_whole,
                     int n_whole_padded, int n_split_units, int splits, float* __restrict__ ws,
-                    int* __restrict__ counters, float c, float* __restrict__ lse,
+                    float c, float* __restrict__ lse, uint16_t* __restrict__ out_lo,
                     int sub_shift) {
   using C = Cfg<T, D>;
   using S = Slot<T, D>;
@@ -113,7 +173,6 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   // entry when the lists name tiles of 2T rows
   __shared__ int2 tl[(T == 128 ? 2 : 1) * C::kThreads];
   __shared__ int wave_count[C::kWaves];
-  __shared__ int arrival;
 
   // Work units: items [0, n_whole) whole, one workgroup each, dispatched
   // first; then each of the remaining items cut into `splits` list segments
@@ -291,9 +350,11 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     // that, p = exp2(s*c - m_run*c) stays under 2^kRescaleSlack, which bf16 P
     // and the fp32 sums hold, and the accumulators are not rescaled.  The
     // result is the same quotient.  NaN differences (-inf to -inf, +inf to
-    // +inf) compare false and keep the offset.
+    // +inf) compare false and keep the offset.  The training variant takes
+    // every rise (slack 0).
+    constexpr float kSlack = kTrain ? 0.0f : kRescaleSlack;
     const float m_new = fmaxf(m_run, mt);
-    const bool raise = (m_new - m_run) * c > kRescaleSlack;
+    const bool raise = (m_new - m_run) * c > kSlack;
     const float m_use = raise ? m_new : m_run;
     const float mc = (m_use == -INFINITY ? 0.0f : m_use) * c;
     const float alpha = raise ? __builtin_amdgcn_exp2f(m_run * c - mc) : 1.0f;
@@ -376,47 +437,6 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     if (j2 >= 0) dma_tile<T, D, true, true>(vh + static_cast<int64_t>(j2) * T * D, vs, wave, v_dma, vk2);
   };
 
-  // Normalise and store the 32 x D rows of this wave (0 for padding query
-  // rows and for rows without keys; NaN when l == 0 or l is NaN).
-  auto store_rows = [&]() {
-    const int64_t ibh = item / num_tiles;
-    const int itile = item - static_cast<int>(ibh) * num_tiles;
-    const int vq = clampi(vbs[itile >> sub_shift] - T * (itile & ((1 << sub_shift) - 1)), 0, T);
-    const int ln = launder(lane);  // per-lane addresses computed here, not hoisted
-    const int row = wave * 32 + (ln & 31);
-    float l_tot;
-    {
-      float lo_half, hi_half;
-      swap_halves(l_run, lo_half, hi_half);
-      l_tot = lo_half + hi_half;
-    }
-    const bool zero_row = !any_keys || row >= vq;
-    const float inv = l_tot != 0.0f ? 1.0f / l_tot : __builtin_nanf("");
-    if (lse != nullptr && ln < 32) {
-      // natural-log log-sum-exp of the scaled logits: (m*c + log2 l) * ln 2,
-      // with the exponent offset m*c taken as 0 while m is -inf (then l is 0
-      // and the result -inf); -inf for padding rows and rows without keys
-      const float mc = (m_run == -INFINITY ? 0.0f : m_run) * c;
-      lse[(ibh * num_tiles + itile) * T + row] =
-          zero_row ? -INFINITY : (mc + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
-    }
-    uint16_t* dst = out + ((ibh * num_tiles + itile) * T + row) * D + 4 * (ln >> 5);
-#pragma unroll
-    for (int db = 0; db < C::kDBlocks; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float x[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = zero_row ? 0.0f : acc[db][4 * g + e] * inv;
-        const bf16x2_t lo2 = to_bf16x2(x[0], x[1]);
-        const bf16x2_t hi2 = to_bf16x2(x[2], x[3]);
-        uint2 pkd;
-        pkd.x = __builtin_bit_cast(unsigned, lo2);
-        pkd.y = __builtin_bit_cast(unsigned, hi2);
-        *reinterpret_cast<uint2*>(dst + 32 * db + 8 * g) = pkd;
-      }
-  };
-
   // The segment in chunks of kThreads list entries; within a chunk the tiles
   // are pipelined (the copies of the next tile overlap the current one).
   for (int base = a; base < end; base += C::kThreads) {
@@ -449,46 +469,55 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   wait_vmcnt<0>();  // Q, when no tile was processed
 
   if (nseg == 1) {  // the whole item: store
-    store_rows();
+    const int64_t ibh = item / num_tiles;
+    store_tile_rows<T, D>(acc, m_run, l_run, any_keys, ibh, item - static_cast<int>(ibh) * num_tiles,
+                          num_tiles, vbs, sub_shift, wave, lane, c, out, lse, out_lo);
     return;
   }
 
-  // ---- a split item: store this segment's partial; the last segment to arrive
-  //      merges all of them, in segment order, and stores the rows ---------------------
+  // ---- a split item: store this segment's partial (merged by the next launch) ---------
   const int ln = launder(lane);
-  {
-    float* slot = ws + static_cast<int64_t>(unit2) * S::kFloats;
+  float* slot = ws + static_cast<int64_t>(unit2) * S::kFloats;
 #pragma unroll
-    for (int db = 0; db < C::kDBlocks; ++db)
+  for (int db = 0; db < C::kDBlocks; ++db)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4)
-        *reinterpret_cast<float4*>(slot + (((wave * C::kDBlocks + db) * 4 + r4) * 64 + ln) * 4) =
-            make_float4(acc[db][4 * r4], acc[db][4 * r4 + 1], acc[db][4 * r4 + 2],
-                        acc[db][4 * r4 + 3]);
-    slot[S::kM + wave * 64 + ln] = m_run;
-    slot[S::kL + wave * 64 + ln] = l_run;
-    if (tid == 0) slot[S::kAny] = any_keys ? 1.0f : 0.0f;
-  }
-  asm volatile("" ::: "memory");  // the stores above stay above the wait
-  wait_vmcnt<0>();  // this thread's partial stores are complete ...
-  __syncthreads();  // ... and so are everyone's, before the arrival is counted
-  int* counter = counters + (item - n_whole);
-  if (tid == 0) arrival = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  if (__builtin_amdgcn_readfirstlane(arrival) != nseg - 1) return;
-  asm volatile("" ::: "memory");  // the loads below stay below the arrival
+    for (int r4 = 0; r4 < 4; ++r4)
+      *reinterpret_cast<float4*>(slot + (((wave * C::kDBlocks + db) * 4 + r4) * 64 + ln) * 4) =
+          make_float4(acc[db][4 * r4], acc[db][4 * r4 + 1], acc[db][4 * r4 + 2],
+                      acc[db][4 * r4 + 3]);
+  slot[S::kM + wave * 64 + ln] = m_run;
+  slot[S::kL + wave * 64 + ln] = l_run;
+  if (tid == 0) slot[S::kAny] = any_keys ? 1.0f : 0.0f;
+}
 
-  // last to arrive: reset the counter for the next launch on this stream, merge
-  if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  float mm = -INFINITY;
-  bool any_all = false;
+// Merge of the split items: one workgroup per item, the same T/32 waves and
+// lane layout as the segments that wrote the item's `splits` slots.  The
+// partials are combined in segment order with the guarded rescaling of the
+// online update (an exponent offset of 0 while the running max is -inf), so
+// the result is a fixed function of the slots; then the rows are stored as
+// for a whole item.
+template <int T, int D>
+__global__ __launch_bounds__(2 * T) void bsa_fwd_merge_kernel(
+    const float* __restrict__ ws, const int32_t* __restrict__ vbs, uint16_t* __restrict__ out,
+    int num_tiles, int n_whole, int splits, float c, float* __restrict__ lse,
+    uint16_t* __restrict__ out_lo, int sub_shift) {
+  using C = Cfg<T, D>;
+  using S = Slot<T, D>;
+  const int m = blockIdx.x;
+  const int item = n_whole + m;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ln = launder(lane);
+  f32x16_t acc[C::kDBlocks];
 #pragma unroll
   for (int db = 0; db < C::kDBlocks; ++db)
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) acc[db][rr] = 0.0f;
-  l_run = 0.0f;
-  for (int sg = 0; sg < nseg; ++sg) {
-    const float* slot = ws + static_cast<int64_t>(unit2 - seg + sg) * S::kFloats;
+  float mm = -INFINITY, l_run = 0.0f;
+  bool any_all = false;
+  for (int sg = 0; sg < splits; ++sg) {
+    const float* slot = ws + (static_cast<int64_t>(m) * splits + sg) * S::kFloats;
     const float ms = slot[S::kM + wave * 64 + ln];
     const float ls = slot[S::kL + wave * 64 + ln];
     const float as = slot[S::kAny];
@@ -511,14 +540,15 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         acc[db][4 * r4 + 3] = acc[db][4 * r4 + 3] * sa + xv.w * sb;
       }
   }
-  any_keys = any_all;
-  m_run = mm;
-  store_rows();
+  const int64_t ibh = item / num_tiles;
+  store_tile_rows<T, D>(acc, mm, l_run, any_all, ibh, item - static_cast<int>(ibh) * num_tiles,
+                        num_tiles, vbs, sub_shift, wave, lane, c, out, lse, out_lo);
 }
 
 template <int T, int D>
 hipError_t launch(const bsa::FwdProblem& p, hipStream_t stream) {
-  const void* fn = reinterpret_cast<const void*>(&bsa_fwd_kernel<T, D>);
+  const void* fn = p.lse != nullptr ? reinterpret_cast<const void*>(&bsa_fwd_kernel<T, D, true>)
+                                    : reinterpret_cast<const void*>(&bsa_fwd_kernel<T, D, false>);
   dim3 block(Cfg<T, D>::kThreads);
   const float c = static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(D))) * kLog2e;
   const uint16_t* q = p.q;
@@ -532,14 +562,20 @@ hipError_t launch(const bsa::FwdProblem& p, hipStream_t stream) {
   int n_whole = p.n_whole, n_whole_padded = (p.n_whole + 7) / 8 * 8;
   int n_split_units = p.n_split_units, splits = p.splits;
   float* ws = p.ws;
-  int* counters = p.counters;
   float cc = c;
   float* lse = p.lse;
+  uint16_t* out_lo = p.out_lo;
   int sub_shift = p.sub_shift;
   void* args[] = {&q, &k, &v, &idx, &num, &vbs, &out, &nt, &ms, &n_whole, &n_whole_padded,
-                  &n_split_units, &splits, &ws, &counters, &cc, &lse, &sub_shift};
+                  &n_split_units, &splits, &ws, &cc, &lse, &out_lo, &sub_shift};
   const int units = n_whole_padded + n_split_units;
-  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(units)), block, args, 0, stream);
+  hipError_t err = hipLaunchKernel(fn, dim3(static_cast<unsigned>(units)), block, args, 0, stream);
+  if (err != hipSuccess || splits <= 1 || n_split_units == 0) return err;
+  const void* merge = reinterpret_cast<const void*>(&bsa_fwd_merge_kernel<T, D>);
+  const float* wsc = ws;
+  void* margs[] = {&wsc, &vbs, &out, &nt, &n_whole, &splits, &cc, &lse, &out_lo, &sub_shift};
+  return hipLaunchKernel(merge, dim3(static_cast<unsigned>(n_split_units / splits)), block, margs,
+                         0, stream);
 }
 
 // Work split.  Workgroups run in rounds of `resident` (occupancy x CUs); the
@@ -548,13 +584,36 @@ hipError_t launch(const bsa::FwdProblem& p, hipStream_t stream) {
 // workgroups: 256 left over), each leftover item's list is cut into
 // s = min(4, resident / leftover) segments, so that the last round is full
 // (256 x 2), as long as every segment keeps at least 4 list positions.
+// Resident workgroups per CU of bsa_fwd_kernel<T, D, *>: a property of the
+// code objects, the same on every gfx950, queried once and kept in an atomic
+// (so that later plans, also those made while a stream is being captured into
+// a graph, make no runtime call).  The smaller of the two variants' counts, so
+// that bsa_fwd and bsa_fwd_lse make the same plan and need the same workspace.
+template <int T, int D>
+hipError_t blocks_per_cu(int* per_cu) {
+  static std::atomic<int> cached{0};
+  int n = cached.load(std::memory_order_acquire);
+  if (n == 0) {
+    int a = 0, b = 0;
+    hipError_t err = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &a, reinterpret_cast<const void*>(&bsa_fwd_kernel<T, D, false>), Cfg<T, D>::kThreads, 0);
+    if (err != hipSuccess) return err;
+    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &b, reinterpret_cast<const void*>(&bsa_fwd_kernel<T, D, true>), Cfg<T, D>::kThreads, 0);
+    if (err != hipSuccess) return err;
+    n = a < b ? a : b;
+    if (n < 1) n = 1;
+    cached.store(n, std::memory_order_release);
+  }
+  *per_cu = n;
+  return hipSuccess;
+}
+
 template <int T, int D>
 hipError_t plan(const bsa::FwdProblem& p, bsa::FwdPlan* plan) {
   int per_cu = 0;
-  const hipError_t err = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      &per_cu, reinterpret_cast<const void*>(&bsa_fwd_kernel<T, D>), Cfg<T, D>::kThreads, 0);
+  const hipError_t err = blocks_per_cu<T, D>(&per_cu);
   if (err != hipSuccess) return err;
-  if (per_cu < 1) per_cu = 1;
   const int64_t resident = static_cast<int64_t>(per_cu) * p.num_cus;
   const int64_t items = p.batch_heads * p.num_tiles;
   const int positions = p.max_sel > 0 ? p.max_sel : 1;
@@ -566,7 +625,6 @@ hipError_t plan(const bsa::FwdProblem& p, bsa::FwdPlan* plan) {
   plan->n_whole = static_cast<int32_t>(s > 1 ? items - left : items);
   plan->n_split_units = static_cast<int32_t>(s > 1 ? left * s : 0);
   plan->ws_bytes = static_cast<size_t>(plan->n_split_units) * Slot<T, D>::kFloats * sizeof(float);
-  plan->counter_bytes = s > 1 ? static_cast<size_t>(left) * sizeof(int) : 0;
   return hipSuccess;
 }
 

@@ -27,8 +27,8 @@ struct FwdProblem {
   int32_t n_split_units;  // the other items, `splits` list segments each
   int32_t splits;
   float* ws;              // n_split_units partial slots (when splits > 1)
-  int32_t* counters;      // one arrival counter per split item, zero between launches
   float* lse;             // [B, H, NT*T] log-sum-exp per row, or null
+  uint16_t* out_lo;       // [B, H, NT*T, D] bf16 rounding residual of out (with lse)
   int32_t sub_shift;      // 1: the lists and lengths count tiles of 2*tile rows
 };
 
@@ -39,10 +39,10 @@ struct FwdPlan {
   int32_t n_split_units;
   int32_t splits;
   size_t ws_bytes;
-  size_t counter_bytes;
 };
 
 hipError_t plan_fwd(const FwdProblem& p, FwdPlan* plan);
+// One launch, or two when items are split (the segments, then their merge).
 hipError_t launch_fwd(const FwdProblem& p, hipStream_t stream);
 
 struct LayoutProblem {
@@ -79,6 +79,7 @@ struct BwdProblem {
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* out;
+  const uint16_t* out_lo;  // bf16 rounding residual of out
   const uint16_t* dout;
   const float* lse;
   const int32_t* q2k_idx;

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_abi_version(lib):
-    assert lib.bsa_abi_version() == 1
+    assert lib.bsa_abi_version() == 2
 
 
 def test_launch_limits_at_the_printed_boundaries(lib):
@@ -94,19 +94,19 @@ def fake(i):
     return ctypes.c_void_p((i + 1) << 28)
 
 
-def fwd_call(lib, tile=128, D=128, B=1, H=1, NT=2, MS=2, ptr=None, idx=None, out=None):
+def fwd_call(lib, tile=128, D=128, B=1, H=1, NT=2, MS=2, ptr=None, idx=None, out=None,
+             ws=NUL, ws_bytes=0):
     q, k, v, num, bs = ((ptr if ptr is not None else fake(i)) for i in range(5))
     idx = fake(5) if idx is None else idx
     out = (ptr if ptr is not None else fake(6)) if out is None else out
-    return lib.bsa_fwd(q, k, v, idx, num, bs, tile, out, B, H, NT, D, MS, NUL)
+    return lib.bsa_fwd(q, k, v, idx, num, bs, tile, out, B, H, NT, D, MS, ws, ws_bytes, NUL)
 
 
-def bwd_call(lib, tile=128, outs=None, ins=None):
-    """bsa_bwd on a 1 x 1 x 2-tile problem with fake pointers (inputs 0..10, outputs 11..14)."""
-    i = [fake(n) for n in range(11)] if ins is None else ins
-    o = [fake(11 + n) for n in range(4)] if outs is None else outs
-    return lib.bsa_bwd(i[0], i[1], i[2], i[3], i[4], i[5], i[6], i[7], i[8], i[9], i[10], tile,
-                       o[0], o[1], o[2], o[3], 1, 1, 2, 128, 2, 2, NUL)
+def bwd_call(lib, tile=128, outs=None, ins=None, B=1, H=1, NT=2):
+    """bsa_bwd on a B x H x NT-tile problem with fake pointers (inputs 0..11, outputs 12..15)."""
+    i = [fake(n) for n in range(12)] if ins is None else ins
+    o = [fake(12 + n) for n in range(4)] if outs is None else outs
+    return lib.bsa_bwd(*i, tile, o[0], o[1], o[2], o[3], B, H, NT, 128, 2, 2, NUL)
 
 
 @pytest.mark.parametrize("tile,D", [(32, 128), (512, 128), (128, 96), (64, 256), (0, 64), (192, 64)])
@@ -139,15 +139,23 @@ def test_outputs_that_overlap_inputs_are_refused(lib):
     q = fake(0)
     # q, k and v may be one tensor
     assert lib.bsa_fwd(q, q, q, fake(5), fake(3), fake(4), 128, fake(6), 1, 1, 2, 128, 2,
-                       NUL) in expected
+                       NUL, 0, NUL) in expected
     lse_on_out = ctypes.c_void_p(fake(6).value + 100)
-    assert lib.bsa_fwd_lse(q, q, q, fake(5), fake(3), fake(4), 128, fake(6), lse_on_out, 1, 1, 2,
-                           128, 2, NUL) == INVALID
-    # backward: dk on dq, delta on dout, dv on the transposed lists
-    o = [fake(11 + n) for n in range(4)]
+    assert lib.bsa_fwd_lse(q, q, q, fake(5), fake(3), fake(4), 128, fake(6), fake(7), lse_on_out,
+                           1, 1, 2, 128, 2, NUL, 0, NUL) == INVALID
+    lo_on_q = ctypes.c_void_p(fake(0).value + 64)
+    assert lib.bsa_fwd_lse(q, q, q, fake(5), fake(3), fake(4), 128, fake(6), lo_on_q, fake(8),
+                           1, 1, 2, 128, 2, NUL, 0, NUL) == INVALID
+    # the workspace must not overlap an input or an output
+    assert fwd_call(lib, ws=fake(1), ws_bytes=4096) == INVALID
+    assert fwd_call(lib, ws=ctypes.c_void_p(fake(6).value + 4096), ws_bytes=4096) == INVALID
+    assert fwd_call(lib, ws=fake(9), ws_bytes=1 << 20) in expected
+    # backward: dk on dq, delta on dout, dv on the transposed lists, dq on out_lo
+    o = [fake(12 + n) for n in range(4)]
     assert bwd_call(lib, outs=[o[0], o[0], o[2], o[3]]) == INVALID
-    assert bwd_call(lib, outs=[o[0], o[1], o[2], fake(4)]) == INVALID
-    assert bwd_call(lib, outs=[o[0], o[1], fake(8), o[3]]) == INVALID
+    assert bwd_call(lib, outs=[o[0], o[1], o[2], fake(5)]) == INVALID
+    assert bwd_call(lib, outs=[o[0], o[1], fake(9), o[3]]) == INVALID
+    assert bwd_call(lib, outs=[fake(4), o[1], o[2], o[3]]) == INVALID
     if not _device_present():
         assert bwd_call(lib) in expected
     # layout and its inverse: a destination on a source or on the map
@@ -163,6 +171,19 @@ def test_outputs_that_overlap_inputs_are_refused(lib):
 def test_fwd_rejects_bad_sizes_and_null_pointers(lib):
     assert fwd_call(lib, B=-1) == INVALID
     assert fwd_call(lib, MS=-1) == INVALID
+    # a workspace needs both its pointer and its size; a negative size is refused
+    assert fwd_call(lib, ws=fake(9), ws_bytes=0) == INVALID
+    assert fwd_call(lib, ws=NUL, ws_bytes=4096) == INVALID
+    assert fwd_call(lib, ws=fake(9), ws_bytes=-1) == INVALID
+    # the training forward needs both statistics outputs
+    q = fake(0)
+    assert lib.bsa_fwd_lse(q, q, q, fake(5), fake(3), fake(4), 128, fake(6), NUL, fake(8),
+                           1, 1, 2, 128, 2, NUL, 0, NUL) == INVALID
+    assert lib.bsa_fwd_lse(q, q, q, fake(5), fake(3), fake(4), 128, fake(6), fake(7), NUL,
+                           1, 1, 2, 128, 2, NUL, 0, NUL) == INVALID
+    ins = [fake(n) for n in range(12)]
+    ins[4] = NUL  # out_lo
+    assert bwd_call(lib, ins=ins) == INVALID
     assert fwd_call(lib, ptr=NUL) == INVALID
     assert fwd_call(lib, idx=NUL) == INVALID
     assert fwd_call(lib, B=1, H=65536) == LIMITS
@@ -202,3 +223,55 @@ def test_without_a_device_launches_fail_cleanly(lib):
 
 def test_shape_helper():
     assert bsa.fwd_out_shape((2, 3, 256, 64)) == (2, 3, 256, 64)
+
+
+def test_workspace_size_validation(lib):
+    n = ctypes.c_int64(-5)
+    assert lib.bsa_fwd_workspace_size(1, 1, 2, 128, 128, 2, None) == INVALID
+    assert lib.bsa_fwd_workspace_size(-1, 1, 2, 128, 128, 2, ctypes.byref(n)) == INVALID
+    assert n.value == 0  # cleared even on error
+    assert lib.bsa_fwd_workspace_size(1, 1, 2, 96, 128, 2, ctypes.byref(n)) == SHAPE
+    assert lib.bsa_fwd_workspace_size(1, 65536, 2, 128, 128, 2, ctypes.byref(n)) == LIMITS
+    assert lib.bsa_fwd_workspace_size(0, 1, 2, 128, 128, 2, ctypes.byref(n)) == OK
+    assert n.value == 0
+    if not _device_present():
+        assert lib.bsa_fwd_workspace_size(1, 1, 2, 128, 128, 2, ctypes.byref(n)) == NO_DEVICE
+
+
+_HUGE_SIZES = """
+import ctypes, sys
+sys.path.insert(0, {root!r})
+import block_sparse_tiled_amd as bsa
+lib = bsa.load()
+F = lambda i: ctypes.c_void_p((i + 1) << 28)
+N = ctypes.c_void_p(0)
+res = []
+for B, H in (({big}, {big}), (1 << 62, 4), (4, 1 << 62), (1 << 31, 1 << 31)):
+    res.append(lib.bsa_fwd(F(0), F(1), F(2), F(3), F(4), F(5), 128, F(6), B, H, 2, 128, 2,
+                           N, 0, N))
+    res.append(lib.bsa_fwd_lse(F(0), F(1), F(2), F(3), F(4), F(5), 128, F(6), F(7), F(8), B, H,
+                               2, 128, 2, N, 0, N))
+    res.append(lib.bsa_bwd(*[F(n) for n in range(12)], 128, F(12), F(13), F(14), F(15), B, H,
+                           2, 128, 2, 2, N))
+    src = (ctypes.c_void_p * 1)(F(0))
+    dst = (ctypes.c_void_p * 1)(F(1))
+    res.append(lib.bsa_tile_layout(src, dst, 1, F(2), 64, B, 64, H, 1, 64, N))
+    res.append(lib.bsa_tile_unlayout(src, dst, 1, F(2), 64, B, 64, H, 1, 64, N))
+    n = ctypes.c_int64(0)
+    res.append(lib.bsa_fwd_workspace_size(B, H, 2, 128, 128, 2, ctypes.byref(n)))
+print(res)
+assert all(r == 3 for r in res), res
+"""
+
+
+def test_overflowing_batch_times_heads_is_refused_not_a_crash():
+    """batch * heads that wraps to 0 (2^32 x 2^32) or overflows int64 must return
+    BSA_ERR_LAUNCH_LIMITS from every entry point; the size checks bound batch*heads by
+    division before forming any product.  Run in a child process, so that a crash
+    (a division by zero) fails this test instead of ending the session."""
+    import subprocess
+    import sys
+
+    code = _HUGE_SIZES.format(root=ROOT, big=1 << 32)
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0, f"rc {res.returncode}: {res.stdout} {res.stderr[-2000:]}"

@@ -290,18 +290,24 @@ def _launch_args(w):
 
 def test_split_lists_back_to_back_shapes_on_one_stream(oracle_mod):
     """Few items with long lists are cut into list segments whose partial results
-    meet in the workspace; two shapes alternate on one stream without a sync, so
-    the second launch reuses counters and slots the first one left behind."""
+    meet in the workspace and are merged by a second launch.  Two shapes alternate on
+    one stream without a sync, all through ONE caller workspace (sized for the larger
+    plan), so every launch overwrites slots the previous one left: the workspace
+    carries nothing from call to call, and repeated calls agree bit for bit."""
     import torch
 
     wa = gen.random_problem(61, B=1, H=2, D=128, T=128, vbs=[128] * 20 + [90], density=0.8)
     wb = gen.random_problem(62, B=2, H=3, D=128, T=128, vbs=[128, 3] + [128] * 30, density=0.6,
                             pad="naninf")
     args_a, args_b = _launch_args(wa), _launch_args(wb)
+    need = max(bsa.workspace_size(x.B, x.H, x.NT, x.T, x.D, x.MS) for x in (wa, wb))
+    assert need > 0, "these shapes are meant to split their lists"
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    ws.fill_(0xFF)  # NaN bit patterns everywhere: nothing may depend on its contents
     outs = []
     for i in range(3):
-        outs.append(("a", bsa.fwd(*args_a, wa.T)))
-        outs.append(("b", bsa.fwd(*args_b, wb.T)))
+        outs.append(("a", bsa.fwd(*args_a, wa.T, workspace=ws)))
+        outs.append(("b", bsa.fwd(*args_b, wb.T, workspace=ws)))
     torch.cuda.synchronize()
     ref = {"a": oracle_out(oracle_mod, wa), "b": oracle_out(oracle_mod, wb)}
     first = {}
@@ -313,8 +319,32 @@ def test_split_lists_back_to_back_shapes_on_one_stream(oracle_mod):
         first.setdefault(name, bits)
 
 
+def test_workspace_choices(oracle_mod):
+    """A shape that splits its lists: with the library's workspace, with none (whole
+    query tiles only, one launch) and with one too small (refused, nothing written).
+    Both runs match the oracle; they may differ only in the last bits."""
+    import torch
+
+    w = gen.random_problem(66, B=1, H=2, D=128, T=128, vbs=[128] * 20 + [90], density=0.8)
+    args = _launch_args(w)
+    need = bsa.workspace_size(w.B, w.H, w.NT, w.T, w.D, w.MS)
+    assert need > 0
+    split = bits_from_dev(bsa.fwd(*args, w.T))
+    whole = bits_from_dev(bsa.fwd(*args, w.T, workspace=None))
+    ref = oracle_out(oracle_mod, w)
+    compare(split, ref, label="split lists")
+    compare(whole, ref, label="whole query tiles")
+    small = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
+    sentinel = torch.full(w.q.shape, 7.0, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(bsa.BsaError) as e:
+        bsa.fwd(*args, w.T, out=sentinel, workspace=small)
+    assert e.value.status == 1
+    torch.cuda.synchronize()
+    assert bool((sentinel == 7.0).all()), "a refused call writes nothing"
+
+
 def test_split_lists_on_two_concurrent_streams(oracle_mod):
-    """Launches on different streams may overlap; each stream has its own workspace."""
+    """Launches on different streams may overlap; each call has its own workspace."""
     import torch
 
     wa = gen.random_problem(63, B=1, H=1, D=128, T=64, vbs=[64] * 40, density=0.9)
@@ -336,13 +366,14 @@ def test_split_lists_on_two_concurrent_streams(oracle_mod):
         compare(bits_from_dev(out), ref[name], label=f"two streams {name}")
 
 
-def test_split_lists_on_many_streams(oracle_mod):
-    """A device keeps at most eight stream workspaces; on further streams a launch
-    that would split its lists runs whole query tiles instead.  Twelve streams,
-    each used twice (concurrently with the others), all match the oracle."""
+def test_same_bits_on_every_stream(oracle_mod):
+    """The output bits do not depend on the stream: the same split shape on twelve
+    streams (used concurrently, each call with its own workspace) gives identical
+    bits on all of them, streams 1 and 12 included."""
     import torch
 
     w = gen.random_problem(65, B=1, H=2, D=128, T=128, vbs=[128] * 20 + [90], density=0.8)
+    assert bsa.workspace_size(w.B, w.H, w.NT, w.T, w.D, w.MS) > 0
     args = _launch_args(w)
     streams = [torch.cuda.Stream() for _ in range(12)]
     for s in streams:
@@ -354,40 +385,44 @@ def test_split_lists_on_many_streams(oracle_mod):
                 outs.append(bsa.fwd(*args, w.T))
     for s in streams:
         s.synchronize()
-    ref = oracle_out(oracle_mod, w)
+    first = bits_from_dev(outs[0])
+    compare(first, oracle_out(oracle_mod, w), label="stream 1")
     for n, out in enumerate(outs):
-        compare(bits_from_dev(out), ref, label=f"stream {n % len(streams)}")
+        np.testing.assert_array_equal(bits_from_dev(out), first,
+                                      err_msg=f"stream {n % len(streams) + 1}")
 
 
 def test_graph_capture_replays_match_eager(oracle_mod):
-    """After a first call on a stream (which makes that stream's workspace), the
-    layout and the forward can be captured into a HIP graph.  The ragged workload
-    splits lists, so the replays also use the workspace counters, which every launch
-    leaves at zero.  Each replay, with eager work and a sync between, gives the eager
-    result bit for bit."""
+    """The layout and the forward captured into a HIP graph on a fresh stream whose
+    FIRST library call happens inside the capture (the ragged workload splits lists,
+    so the capture holds the segment launch, the merge launch and a workspace from
+    the graph's memory pool).  Each replay, with eager work and a sync between, gives
+    the eager result bit for bit."""
     import torch
 
     w = gen.ragged(gate=True)
+    assert bsa.workspace_size(w.B, w.H, w.NT, w.T, w.D, w.MS) > 0
     tok = [to_dev(w.tok[x]) for x in ("q", "k", "v", "gate")]
     src = to_dev(w.tile_src_token)
     idx, num, vbs = to_dev(w.q2k_idx), to_dev(w.q2k_num), to_dev(w.vbs)
     tiled = [torch.empty((w.B, w.H, w.S, w.D), dtype=torch.bfloat16, device="cuda") for _ in tok]
     out = torch.empty((w.B, w.H, w.S, w.D), dtype=torch.bfloat16, device="cuda")
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
 
     def step():
         bsa.tile_layout(tok, src, w.T, outs=tiled)
         bsa.fwd(tiled[0], tiled[1], tiled[2], idx, num, vbs, w.T, out=out)
 
-    with torch.cuda.stream(side):
-        step()  # first call on this stream: its workspace is made here, outside the capture
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        step()  # the first call on this stream
+    torch.cuda.synchronize()
+    step()  # eager, on the default stream
     torch.cuda.synchronize()
     eager = bits_from_dev(out)
     compare(eager, oracle_out(oracle_mod, w), label="eager ragged")
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=side):
-        step()
     for r in range(4):
         out.fill_(float("nan"))
         for t in tiled:
@@ -396,7 +431,6 @@ def test_graph_capture_replays_match_eager(oracle_mod):
         graph.replay()
         torch.cuda.synchronize()
         np.testing.assert_array_equal(bits_from_dev(out), eager, err_msg=f"replay {r}")
-        # eager launches between replays share the stream's workspace
         with torch.cuda.stream(side):
             step()
         torch.cuda.synchronize()
@@ -423,7 +457,7 @@ def test_tile_256_duplicates_and_lse(oracle_mod):
     w.q2k_num[1, 0, 2] = 0
     print("fwd tile 256 duplicates + lse", flush=True)
     q, k, v = (to_dev(x) for x in (w.q, w.k, w.v))
-    out, lse = bsa.fwd_lse(q, k, v, to_dev(w.q2k_idx), to_dev(w.q2k_num), to_dev(w.vbs), T)
+    out, lse, _ = bsa.fwd_lse(q, k, v, to_dev(w.q2k_idx), to_dev(w.q2k_num), to_dev(w.vbs), T)
     compare(bits_from_dev(out), oracle_out(oracle_mod, w), label="tile 256 duplicates")
     _, lse64 = oracle.fwd64(w.q, w.k, w.v, w.q2k_idx, w.q2k_num, w.vbs, T)
     got = lse.cpu().numpy()

@@ -78,10 +78,10 @@ def run_path(tok, src_map, T, idx, num, vbs, dout_seed):
 
     q, k, v, *rest = bsa.tile_layout(tok, to_dev(src_map), T)
     d_idx, d_num, d_vbs = to_dev(idx), to_dev(num), to_dev(vbs)
-    out, lse = bsa.fwd_lse(q, k, v, d_idx, d_num, d_vbs, T)
+    out, lse, out_lo = bsa.fwd_lse(q, k, v, d_idx, d_num, d_vbs, T)
     k2q_idx, k2q_num = bsa.bwd_k2q(d_idx, d_num)
     dout = randn_bf16(tuple(q.shape), dout_seed)
-    dq, dk, dv = bsa.bwd(q, k, v, out, dout, lse, d_idx, d_num, k2q_idx, k2q_num, d_vbs, T)
+    dq, dk, dv = bsa.bwd(q, k, v, out, out_lo, dout, lse, d_idx, d_num, k2q_idx, k2q_num, d_vbs, T)
     torch.cuda.synchronize()
     return dict(q=q, k=k, v=v, out=out, lse=lse, dout=dout, dq=dq, dk=dk, dv=dv, rest=rest)
 
