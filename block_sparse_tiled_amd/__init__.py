@@ -7,6 +7,9 @@ from .api import (  # noqa: F401
     BsaError,
     bwd,
     bwd_k2q,
+    coarse,
+    coarse_combine,
+    coarse_workspace_size,
     cube_tile_map,
     fwd,
     fwd_lse,

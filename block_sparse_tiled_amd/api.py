@@ -76,6 +76,13 @@ def load():
     ip = ctypes.POINTER(ctypes.c_int32)
     lib.bsa_cube_tile_map.argtypes = [i64, i64, i64, i32, i32, i32, i32, ip, ip, ip]
     lib.bsa_cube_tile_map.restype = ctypes.c_int
+    lib.bsa_coarse_workspace_size.argtypes = [i64, i64, i64, i32, i32, ctypes.POINTER(i64)]
+    lib.bsa_coarse_workspace_size.restype = ctypes.c_int
+    lib.bsa_coarse.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, i64, i64, i64, i32, i32, vp,
+                               i64, vp]
+    lib.bsa_coarse.restype = ctypes.c_int
+    lib.bsa_coarse_combine.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, i32, vp]
+    lib.bsa_coarse_combine.restype = ctypes.c_int
     lib.bsa_status_string.argtypes = [ctypes.c_int]
     lib.bsa_status_string.restype = ctypes.c_char_p
     lib.bsa_abi_version.argtypes = []
@@ -415,3 +422,88 @@ def bwd(q, k, v, out, out_lo, dout, lse, q2k_idx, q2k_num, k2q_idx, k2q_num, blo
                            _ptr(grads[2]), _ptr(delta), B, H, NT, D, int(q2k_idx.shape[3]),
                            int(k2q_idx.shape[3]), _stream_handle(device)))
     return tuple(grads)
+
+
+COARSE_MAX_TILES = 4096  # mirrored from include/bsa.h
+
+
+def coarse_workspace_size(batch, heads, num_tiles, tile, head_dim):
+    """Bytes of workspace ``coarse`` needs."""
+    lib = load()
+    n = ctypes.c_int64(0)
+    _check(lib.bsa_coarse_workspace_size(batch, heads, num_tiles, tile, head_dim, ctypes.byref(n)))
+    return int(n.value)
+
+
+def coarse(q, k, v, block_sizes, tile, topk, max_sel=None, coarse_out=True, q2k_idx=None,
+           q2k_num=None, workspace=None):
+    """Coarse stage on tiled q, k, v [B, H, NT*tile, D] (bf16, cuda): each query tile's key
+    tiles and the coarse output.  Returns (q2k_idx int32 [B, H, NT, max_sel], q2k_num int32
+    [B, H, NT], coarse_out float32 [B, H, NT, D] or None).  ``max_sel`` defaults to topk."""
+    import torch
+
+    lib = load()
+    device = q.device
+    if device.type != "cuda":
+        raise ValueError("the coarse stage runs on a GPU: q must be a cuda tensor")
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, name, torch.bfloat16, device, 4)
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k and v must have the same shape")
+    B, H, S, D = q.shape
+    if tile not in TILES or S % tile:
+        raise ValueError(f"tile must be 64, 128 or 256 and divide the sequence ({S})")
+    NT = S // tile
+    _require(block_sizes, "block_sizes", torch.int32, device, 1)
+    if tuple(block_sizes.shape) != (NT,):
+        raise ValueError("block_sizes must be [NT]")
+    MS = int(topk if max_sel is None else max_sel)
+    if q2k_idx is None:
+        q2k_idx = torch.empty((B, H, NT, MS), dtype=torch.int32, device=device)
+    if q2k_num is None:
+        q2k_num = torch.empty((B, H, NT), dtype=torch.int32, device=device)
+    _require(q2k_idx, "q2k_idx", torch.int32, device, 4)
+    _require(q2k_num, "q2k_num", torch.int32, device, 3)
+    if tuple(q2k_idx.shape) != (B, H, NT, MS) or tuple(q2k_num.shape) != (B, H, NT):
+        raise ValueError("q2k_idx must be [B, H, NT, max_sel] and q2k_num [B, H, NT]")
+    oc = None
+    if coarse_out is True:
+        oc = torch.empty((B, H, NT, D), dtype=torch.float32, device=device)
+    elif coarse_out is not None and coarse_out is not False:
+        oc = coarse_out
+        _require(oc, "coarse_out", torch.float32, device, 4)
+        if tuple(oc.shape) != (B, H, NT, D):
+            raise ValueError("coarse_out must be [B, H, NT, D]")
+    with torch.cuda.device(device):
+        need = coarse_workspace_size(B, H, NT, tile, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    _require(workspace, "workspace", torch.uint8, device, 1)
+    with torch.cuda.device(device):
+        _check(lib.bsa_coarse(_ptr(q), _ptr(k), _ptr(v), _ptr(block_sizes), tile, int(topk),
+                              _ptr(q2k_idx), _ptr(q2k_num), _ptr(oc), B, H, NT, D, MS,
+                              _ptr(workspace), workspace.numel(), _stream_handle(device)))
+    return q2k_idx, q2k_num, oc
+
+
+def coarse_combine(out, gate, coarse_out, block_sizes, tile):
+    """In place: out = out + gate * coarse output of each valid row's tile (bf16, one
+    rounding); padding rows keep their value.  Returns ``out``."""
+    import torch
+
+    lib = load()
+    device = out.device
+    _require(out, "out", torch.bfloat16, device, 4)
+    _require(gate, "gate", torch.bfloat16, device, 4)
+    _require(coarse_out, "coarse_out", torch.float32, device, 4)
+    _require(block_sizes, "block_sizes", torch.int32, device, 1)
+    B, H, S, D = out.shape
+    if gate.shape != out.shape or tile not in TILES or S % tile:
+        raise ValueError("gate must have out's shape and tile divide the sequence")
+    NT = S // tile
+    if tuple(coarse_out.shape) != (B, H, NT, D) or tuple(block_sizes.shape) != (NT,):
+        raise ValueError("coarse_out must be [B, H, NT, D] and block_sizes [NT]")
+    with torch.cuda.device(device):
+        _check(lib.bsa_coarse_combine(_ptr(out), _ptr(gate), _ptr(coarse_out), _ptr(block_sizes),
+                                      tile, B, H, NT, D, _stream_handle(device)))
+    return out

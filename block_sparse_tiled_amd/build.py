@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbsa.so")
-SOURCES = ["bsa_api.hip", "bsa_fwd.hip", "bsa_layout.hip", "bsa_bwd.hip"]
+SOURCES = ["bsa_api.hip", "bsa_fwd.hip", "bsa_layout.hip", "bsa_bwd.hip", "bsa_coarse.hip"]
 ARCH = "gfx950"
 
 

@@ -1,0 +1,405 @@
+// Coarse stage of video sparse attention for gfx950 (AMD Instinct MI355X):
+// the choice of each query tile's key tiles (q2k_idx, q2k_num) and the coarse
+// output, and the gated sum of the coarse and fine outputs.
+//
+// FastVideo fastvideo-kernel commit list, page 3: the hardening commit names
+// the block-sparse kernel the "fine" attention (its fine-attention override)
+// and the fused-layout commit scatters a gate into the tile buffer with Q, K
+// and V; neither says how the tile lists are chosen.  The definition taken is
+// the coarse stage of Video Sparse Attention (Zhang et al., 2025):
+//   - every tile becomes one token, the mean of its valid rows;
+//   - the pooled queries attend to the pooled keys; each query tile keeps the
+//     topk key tiles with the largest coarse logits (a NaN logit ranks as
+//     -inf, -0 as +0, equal logits by ascending index), listed by ascending
+//     index, unused list entries -1; an empty query tile keeps nothing;
+//   - the coarse output of a query tile is that pooled attention's result,
+//     over every non-empty key tile;
+//   - the layer output is the fine output plus the gate times the coarse
+//     output of the token's tile.
+// The pooled means and the logits are binary32 in a fixed order (rows summed
+// in order then one division; products and sums over d ascending, never
+// fused), so the selection is a fixed function of the inputs, reproducible
+// bit for bit by a plain CPU loop.
+//
+// Kernels (all memory- or latency-bound; the stage is small next to the fine
+// attention: for the video shape it reads Q, K and V once):
+//   - coarse_pool_kernel: one thread per (tensor, head, tile, 16-byte chunk
+//     of a row), summing the tile's valid rows in order (8 columns each);
+//   - coarse_logits_kernel: the NT x NT logits per head, 64 x 64 per
+//     workgroup, each thread 4 x 4 of them, d ascending through LDS;
+//   - coarse_select_kernel: one wave per query tile; the row's keys in
+//     registers, the k-th largest found by a 32-step bisection on their
+//     order-preserving integer images (one ballot count per step), then the
+//     kept tiles written in ascending order through ballot prefix counts;
+//     also turns the row into softmax weights for the coarse output;
+//   - coarse_out_kernel: those weights times the pooled values;
+//   - coarse_combine_kernel: out += gate * coarse output, valid rows only.
+#include <hip/hip_runtime.h>
+
+#include "bsa_fwd_common.h"
+#include "bsa_launch.h"
+
+namespace {
+
+using namespace bsa::detail;
+
+// ---- pooling ------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void coarse_pool_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ vbs, int num_tiles, int tile, int64_t tiles_all,
+    float* __restrict__ pooled) {
+  constexpr int kChunks = D / 8;
+  const int64_t total = 3 * tiles_all * kChunks;
+  for (int64_t g = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; g < total;
+       g += static_cast<int64_t>(gridDim.x) * 256) {
+  const int64_t u = g / kChunks;  // (tensor, bh, t)
+  const int c = static_cast<int>(g - u * kChunks);
+  const int x = static_cast<int>(u / tiles_all);
+  const int64_t rest = u - x * tiles_all;  // bh * NT + t
+  const int t = static_cast<int>(rest % num_tiles);
+  const uint16_t* src = (x == 0 ? q : (x == 1 ? k : v)) + rest * tile * D + 8 * c;
+  const int n = clampi(vbs[t], 0, tile);
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+#pragma unroll 8
+  for (int s = 0; s < n; ++s) {
+    const uint4 w = *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(s) * D);
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] = __fadd_rn(acc[2 * e], __uint_as_float(ww[e] << 16));
+      acc[2 * e + 1] = __fadd_rn(acc[2 * e + 1], __uint_as_float(ww[e] & 0xffff0000u));
+    }
+  }
+  float* dst = pooled + u * D + 8 * c;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) dst[e] = n > 0 ? __fdiv_rn(acc[e], static_cast<float>(n)) : 0.0f;
+  }
+}
+
+// ---- logits: g[bh][i][j] = sum_d qm[bh][i][d] * km[bh][j][d], d ascending, no fusing --------
+// 64 x 64 logits per workgroup of 256 threads; thread (ty, tx) owns rows ty + 16a and
+// columns tx + 16b (a, b < 4).  The pooled rows pass through LDS 32 columns of d at a
+// time, transposed (d-major) so that a thread's four rows (columns) are 16 apart.
+template <int D>
+__global__ __launch_bounds__(256) void coarse_logits_kernel(const float* __restrict__ qm,
+                                                            const float* __restrict__ km,
+                                                            int num_tiles,
+                                                            float* __restrict__ logits) {
+  __shared__ float qs[32][65];
+  __shared__ float ks[32][65];
+  const int bh = blockIdx.z;
+  const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const float* qh = qm + static_cast<int64_t>(bh) * num_tiles * D;
+  const float* kh = km + static_cast<int64_t>(bh) * num_tiles * D;
+  float acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0f;
+  for (int d0 = 0; d0 < D; d0 += 32) {
+    // 64 rows x 32 columns of each operand: 8 values per thread
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int idx = tid + 256 * e;  // 0 .. 2047
+      const int row = idx >> 5, dd = idx & 31;
+      const int i = i0 + row, j = j0 + row;
+      qs[dd][row] = i < num_tiles ? qh[static_cast<int64_t>(i) * D + d0 + dd] : 0.0f;
+      ks[dd][row] = j < num_tiles ? kh[static_cast<int64_t>(j) * D + d0 + dd] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int dd = 0; dd < 32; ++dd) {
+      float qa[4], kb[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) qa[a] = qs[dd][ty + 16 * a];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) kb[b] = ks[dd][tx + 16 * b];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = __fadd_rn(acc[a][b], __fmul_rn(qa[a], kb[b]));
+    }
+    __syncthreads();
+  }
+  float* out = logits + static_cast<int64_t>(bh) * num_tiles * num_tiles;
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int i = i0 + ty + 16 * a;
+    if (i >= num_tiles) continue;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int j = j0 + tx + 16 * b;
+      if (j < num_tiles) out[static_cast<int64_t>(i) * num_tiles + j] = acc[a][b];
+    }
+  }
+}
+
+// ---- selection ------------------------------------------------------------------------
+// Order-preserving image of a logit as an unsigned integer: a NaN ranks as -inf and -0
+// as +0, and larger logits map to larger integers (0 is below every logit's image).
+__device__ __forceinline__ uint32_t rank_image(float g) {
+  if (g != g) g = -INFINITY;
+  if (g == 0.0f) g = 0.0f;
+  const uint32_t b = __float_as_uint(g);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ int popc(uint64_t m) { return __popcll(m); }
+
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
+}
+
+// One wave per (bh, query tile i); key tile j = lane + 64 r is held in register r.
+// Writes the list and the count, and (when weights are wanted) overwrites the logits
+// row with the softmax weights of the coarse output: p_j / l over the non-empty key
+// tiles, 0 elsewhere (all 0 for an empty query tile or one without candidates).
+template <int KPL>
+__global__ __launch_bounds__(256) void coarse_select_kernel(
+    float* __restrict__ logits, const int32_t* __restrict__ vbs, int num_tiles, int64_t rows,
+    int topk, int max_sel, float scale, int32_t* __restrict__ q2k_idx,
+    int32_t* __restrict__ q2k_num, int weights) {
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;  // whole waves leave together
+  const int i = static_cast<int>(row % num_tiles);
+  float* grow = logits + row * num_tiles;
+  int32_t* list = q2k_idx + row * max_sel;
+  const bool q_valid = vbs[i] > 0;
+
+  float gv[KPL];
+  uint32_t key[KPL];
+  int n_valid = 0;
+#pragma unroll
+  for (int r = 0; r < KPL; ++r) {
+    const int j = lane + 64 * r;
+    const bool ok = q_valid && j < num_tiles && vbs[j] > 0;
+    gv[r] = ok ? grow[j] : 0.0f;
+    key[r] = ok ? rank_image(gv[r]) : 0u;
+    n_valid += popc(__ballot(ok));
+  }
+  const int k = topk < n_valid ? topk : n_valid;
+
+  int written = 0;
+  if (k > 0) {
+    // the k-th largest image: the largest tau with #{key >= tau} >= k
+    uint32_t tau = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = tau | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int r = 0; r < KPL; ++r) cnt += popc(__ballot(key[r] >= cand));
+      if (cnt >= k) tau = cand;
+    }
+    int above = 0;
+#pragma unroll
+    for (int r = 0; r < KPL; ++r) above += popc(__ballot(key[r] > tau));
+    const int need = k - above;  // >= 1: how many of the tiles at tau are kept
+    int eq_before = 0;
+#pragma unroll
+    for (int r = 0; r < KPL; ++r) {
+      const bool eq = key[r] == tau;  // tau > 0, so never an empty or absent tile
+      const uint64_t meq = __ballot(eq);
+      const bool sel = key[r] > tau || (eq && eq_before + lanes_below(meq) < need);
+      eq_before += popc(meq);
+      const uint64_t msel = __ballot(sel);
+      if (sel) list[written + lanes_below(msel)] = lane + 64 * r;
+      written += popc(msel);
+    }
+  }
+  for (int n = written + lane; n < max_sel; n += 64) list[n] = -1;
+  if (lane == 0) q2k_num[row] = written;
+
+  if (!weights) return;
+  // softmax weights over the non-empty key tiles (a NaN logit is NaN here, as the
+  // plain formula propagates it)
+  float m = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < KPL; ++r)
+    if (key[r] != 0u) m = fmaxf(m, scale * gv[r]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  float p[KPL], l = 0.0f;
+#pragma unroll
+  for (int r = 0; r < KPL; ++r) {
+    p[r] = key[r] != 0u ? __expf(scale * gv[r] - m) : 0.0f;
+    l += p[r];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
+  const bool any = n_valid > 0;
+#pragma unroll
+  for (int r = 0; r < KPL; ++r) {
+    const int j = lane + 64 * r;
+    if (j < num_tiles) grow[j] = any ? p[r] / l : 0.0f;
+  }
+}
+
+// ---- coarse output: oc[bh][i][:] = sum_j w[bh][i][j] * vm[bh][j][:] -----------------------
+// 64 query tiles x 64 columns per workgroup (thread: 4 x 4), j through LDS 32 at a time.
+template <int D>
+__global__ __launch_bounds__(256) void coarse_out_kernel(const float* __restrict__ w,
+                                                         const float* __restrict__ vm,
+                                                         int num_tiles, float* __restrict__ oc) {
+  __shared__ float ws[32][65];
+  __shared__ float vs[32][65];
+  const int bh = blockIdx.z;
+  const int i0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const float* wh = w + static_cast<int64_t>(bh) * num_tiles * num_tiles;
+  const float* vh = vm + static_cast<int64_t>(bh) * num_tiles * D;
+  float acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0f;
+  for (int j0 = 0; j0 < num_tiles; j0 += 32) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int idx = tid + 256 * e;
+      const int row = idx >> 5, jj = idx & 31;  // weights: row i0 + row, column j0 + jj
+      const int i = i0 + row, j = j0 + jj;
+      ws[jj][row] = (i < num_tiles && j < num_tiles) ? wh[static_cast<int64_t>(i) * num_tiles + j]
+                                                     : 0.0f;
+      const int vr = idx >> 6, vc = idx & 63;  // values: row j0 + vr, column c0 + vc
+      const int jv = j0 + vr;
+      if (vr < 32) vs[vr][vc] = jv < num_tiles ? vh[static_cast<int64_t>(jv) * D + c0 + vc] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int jj = 0; jj < 32; ++jj) {
+      float wa[4], vb[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) wa[a] = ws[jj][ty + 16 * a];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) vb[b] = vs[jj][tx + 16 * b];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] += wa[a] * vb[b];
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int i = i0 + ty + 16 * a;
+    if (i >= num_tiles) continue;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      oc[(static_cast<int64_t>(bh) * num_tiles + i) * D + c0 + tx + 16 * b] = acc[a][b];
+  }
+}
+
+// ---- out += gate * coarse output of the row's tile (valid rows only) ----------------------
+template <int D>
+__global__ __launch_bounds__(256) void coarse_combine_kernel(uint16_t* __restrict__ out,
+                                                             const uint16_t* __restrict__ gate,
+                                                             const float* __restrict__ oc,
+                                                             const int32_t* __restrict__ vbs,
+                                                             int num_tiles, int tile,
+                                                             int64_t rows) {
+  constexpr int kChunks = D / 8;
+  const int64_t total = rows * kChunks;
+  for (int64_t g = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; g < total;
+       g += static_cast<int64_t>(gridDim.x) * 256) {
+  const int64_t row = g / kChunks;
+  const int c = static_cast<int>(g - row * kChunks);
+  const int64_t bht = row / tile;  // bh * NT + t
+  const int t = static_cast<int>(bht % num_tiles);
+  if (static_cast<int>(row - bht * tile) >= clampi(vbs[t], 0, tile)) continue;  // padding stays +0
+  uint4* po = reinterpret_cast<uint4*>(out + row * D + 8 * c);
+  const uint4 o = *po;
+  const uint4 gt = *reinterpret_cast<const uint4*>(gate + row * D + 8 * c);
+  const float* cv = oc + bht * D + 8 * c;
+  const uint32_t ow[4] = {o.x, o.y, o.z, o.w}, gw[4] = {gt.x, gt.y, gt.z, gt.w};
+  uint32_t res[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float lo = __uint_as_float(ow[e] << 16) + __uint_as_float(gw[e] << 16) * cv[2 * e];
+    const float hi = __uint_as_float(ow[e] & 0xffff0000u) +
+                     __uint_as_float(gw[e] & 0xffff0000u) * cv[2 * e + 1];
+    res[e] = __builtin_bit_cast(uint32_t, to_bf16x2(lo, hi));
+  }
+  *po = make_uint4(res[0], res[1], res[2], res[3]);
+  }
+}
+
+// Grid of a grid-stride launch over `threads` work items, 256 per workgroup.
+unsigned stride_grid(int64_t threads) {
+  const int64_t blocks = (threads + 255) / 256;
+  return static_cast<unsigned>(blocks < (int64_t{1} << 20) ? (blocks > 0 ? blocks : 1) : (int64_t{1} << 20));
+}
+
+template <int D>
+hipError_t launch_coarse_d(const bsa::CoarseProblem& p, hipStream_t stream) {
+  const int64_t tiles_all = p.batch_heads * p.num_tiles;
+  float* qm = p.ws;
+  float* km = qm + tiles_all * D;
+  float* vm = km + tiles_all * D;
+  float* logits = vm + tiles_all * D;
+  {
+    const int64_t threads = 3 * tiles_all * (D / 8);
+    hipLaunchKernelGGL(coarse_pool_kernel<D>, dim3(stride_grid(threads)),
+                       dim3(256), 0, stream, p.q, p.k, p.v, p.block_sizes, p.num_tiles, p.tile,
+                       tiles_all, qm);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  const unsigned nb = static_cast<unsigned>((p.num_tiles + 63) / 64);
+  hipLaunchKernelGGL(coarse_logits_kernel<D>, dim3(nb, nb, static_cast<unsigned>(p.batch_heads)),
+                     dim3(256), 0, stream, qm, km, p.num_tiles, logits);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const float scale = static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(D)));
+  const int weights = p.coarse_out != nullptr ? 1 : 0;
+  const dim3 sgrid(static_cast<unsigned>((tiles_all + 3) / 4));
+  if (p.num_tiles <= 256)
+    hipLaunchKernelGGL(coarse_select_kernel<4>, sgrid, dim3(256), 0, stream, logits,
+                       p.block_sizes, p.num_tiles, tiles_all, p.topk, p.max_sel, scale, p.q2k_idx,
+                       p.q2k_num, weights);
+  else if (p.num_tiles <= 1024)
+    hipLaunchKernelGGL(coarse_select_kernel<16>, sgrid, dim3(256), 0, stream, logits,
+                       p.block_sizes, p.num_tiles, tiles_all, p.topk, p.max_sel, scale, p.q2k_idx,
+                       p.q2k_num, weights);
+  else
+    hipLaunchKernelGGL(coarse_select_kernel<64>, sgrid, dim3(256), 0, stream, logits,
+                       p.block_sizes, p.num_tiles, tiles_all, p.topk, p.max_sel, scale, p.q2k_idx,
+                       p.q2k_num, weights);
+  err = hipGetLastError();
+  if (err != hipSuccess || !weights) return err;
+  hipLaunchKernelGGL(coarse_out_kernel<D>,
+                     dim3(D / 64, nb, static_cast<unsigned>(p.batch_heads)), dim3(256), 0, stream,
+                     logits, vm, p.num_tiles, p.coarse_out);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+namespace bsa {
+
+size_t coarse_workspace_bytes(int64_t batch_heads, int64_t num_tiles, int32_t head_dim) {
+  return static_cast<size_t>(batch_heads) * static_cast<size_t>(num_tiles) *
+         (3 * static_cast<size_t>(head_dim) + static_cast<size_t>(num_tiles)) * sizeof(float);
+}
+
+hipError_t launch_coarse(const CoarseProblem& p, hipStream_t stream) {
+  return p.head_dim == 128 ? launch_coarse_d<128>(p, stream) : launch_coarse_d<64>(p, stream);
+}
+
+hipError_t launch_coarse_combine(const CombineProblem& p, hipStream_t stream) {
+  const dim3 grid(stride_grid(p.rows * (p.head_dim / 8)));
+  if (p.head_dim == 128)
+    hipLaunchKernelGGL(coarse_combine_kernel<128>, grid, dim3(256), 0, stream, p.out, p.gate,
+                       p.coarse_out, p.block_sizes, p.num_tiles, p.tile, p.rows);
+  else
+    hipLaunchKernelGGL(coarse_combine_kernel<64>, grid, dim3(256), 0, stream, p.out, p.gate,
+                       p.coarse_out, p.block_sizes, p.num_tiles, p.tile, p.rows);
+  return hipGetLastError();
+}
+
+}  // namespace bsa

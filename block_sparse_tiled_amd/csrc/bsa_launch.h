@@ -102,6 +102,40 @@ struct BwdProblem {
 
 hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream);
 
+// The coarse stage: tile selection and the coarse output.
+struct CoarseProblem {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* block_sizes;
+  int32_t* q2k_idx;   // [B, H, NT, max_sel]
+  int32_t* q2k_num;   // [B, H, NT]
+  float* coarse_out;  // [B, H, NT, D], or null
+  float* ws;          // coarse_workspace_bytes()
+  int64_t batch_heads;
+  int32_t num_tiles;
+  int32_t tile;
+  int32_t head_dim;
+  int32_t topk;
+  int32_t max_sel;
+};
+
+size_t coarse_workspace_bytes(int64_t batch_heads, int64_t num_tiles, int32_t head_dim);
+hipError_t launch_coarse(const CoarseProblem& p, hipStream_t stream);
+
+struct CombineProblem {
+  uint16_t* out;           // [B, H, NT*T, D], updated in place
+  const uint16_t* gate;    // [B, H, NT*T, D]
+  const float* coarse_out; // [B, H, NT, D]
+  const int32_t* block_sizes;
+  int32_t num_tiles;
+  int32_t tile;
+  int32_t head_dim;
+  int64_t rows;  // B*H*NT*T
+};
+
+hipError_t launch_coarse_combine(const CombineProblem& p, hipStream_t stream);
+
 // The inverse gather: p.src are tile buffers, p.dst token-major outputs, and
 // p.tile_src_token holds the tile row of every token (token_row).
 hipError_t launch_tile_unlayout(const LayoutProblem& p, hipStream_t stream);

@@ -1,0 +1,154 @@
+"""GPU parity of the coarse stage (bsa_coarse, bsa_coarse_combine) against the oracle.
+
+The kept tile lists and counts are compared bit for bit: the pooled means and the
+logits are binary32 in the same fixed order on both sides (parity of the definition is
+unpinned by the pages, which do not describe this stage; the oracle's own pins are in
+test_oracle_coarse_pins.py).  The coarse output is compared within 1e-4 of its scale
+(fp32 sums in another order and the GPU's exponential), and the gated layer output
+out + gate * coarse with the forward's bar.
+"""
+import numpy as np
+import pytest
+
+import block_sparse_tiled_amd as bsa
+from block_sparse_tiled_amd import inputs as gen
+from parity import bits_from_dev, compare, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    bsa.load()
+
+
+def run_coarse(q, k, v, vbs, T, topk, max_sel=None):
+    import torch
+
+    idx, num, oc = bsa.coarse(to_dev(q), to_dev(k), to_dev(v), to_dev(vbs), T, topk,
+                              max_sel=max_sel)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), num.cpu().numpy(), oc.cpu().numpy()
+
+
+def check(q, k, v, vbs, T, topk, max_sel=None, label=""):
+    import oracle
+
+    got_idx, got_num, got_oc = run_coarse(q, k, v, vbs, T, topk, max_sel)
+    ref_idx, ref_num, ref_oc = oracle.coarse(q, k, v, vbs, T, topk, max_sel)
+    np.testing.assert_array_equal(got_num, ref_num, err_msg=f"{label}: counts")
+    np.testing.assert_array_equal(got_idx, ref_idx, err_msg=f"{label}: lists")
+    assert np.array_equal(np.isnan(got_oc), np.isnan(ref_oc)), f"{label}: coarse NaN mask"
+    fin = np.isfinite(ref_oc)
+    scale = max(1.0, float(np.abs(ref_oc[fin]).max())) if fin.any() else 1.0
+    err = float(np.abs(got_oc[fin] - ref_oc[fin]).max()) if fin.any() else 0.0
+    print(f"{label}: lists equal, coarse output max |diff| {err:.2e}", flush=True)
+    assert err <= 1e-4 * scale, f"{label}: coarse output max |diff| {err:.3e}"
+    return ref_idx, ref_num, ref_oc
+
+
+def randn(rng, shape, sigma=1.0):
+    return gen.to_bf16_bits((sigma * rng.standard_normal(shape)).astype(np.float32))
+
+
+@pytest.mark.parametrize("T,D,NT,topk", [(64, 64, 8, 3), (64, 128, 40, 7), (128, 128, 17, 17),
+                                         (128, 64, 300, 25), (256, 128, 9, 4), (64, 128, 1100, 40),
+                                         (128, 128, 5, 0)])
+def test_random_problems(T, D, NT, topk):
+    """NT past 256 and past 1024 reach the wider register blocks of the selection."""
+    rng = np.random.default_rng(T + D + NT)
+    vbs = rng.integers(0, T + 1, NT).astype(np.int32)
+    vbs[rng.random(NT) < 0.15] = 0
+    vbs[0] = T
+    B, H = (1, 2) if NT > 200 else (2, 3)
+    q, k, v = (randn(rng, (B, H, NT * T, D)) for _ in range(3))
+    # padding rows hold NaN / Inf: never read
+    pad = (np.arange(NT * T) % T) >= np.repeat(vbs, T)
+    for x in (q, k, v):
+        x[:, :, pad] = 0x7FC0
+    print(f"coarse T={T} D={D} NT={NT} topk={topk}", flush=True)
+    check(q, k, v, vbs, T, topk, max_sel=topk + 3, label=f"T={T} D={D} NT={NT} topk={topk}")
+
+
+def test_ties_nan_and_every_tile():
+    """Copies of one key tile give equal logits (the lower index is kept); a NaN in a
+    valid key row ranks that tile as -inf; topk above the tile count keeps every
+    non-empty tile."""
+    rng = np.random.default_rng(5)
+    T, D, NT = 64, 128, 12
+    vbs = np.array([64, 64, 64, 0, 64, 64, 30, 64, 64, 64, 1, 64], np.int32)
+    q, k, v = (randn(rng, (1, 2, NT * T, D)) for _ in range(3))
+    for t in (4, 7, 9):  # tiles 4, 7 and 9 equal tile 1: tied logits
+        k[:, :, t * T:(t + 1) * T] = k[:, :, T:2 * T]
+    k[:, 1, 5 * T + 3, 7] = 0x7FC0  # a NaN in a valid row of tile 5, head 1
+    for topk in (1, 2, 4, 6, 11, 20):
+        check(q, k, v, vbs, T, topk, max_sel=20, label=f"ties topk={topk}")
+
+
+def test_video_config_full_size():
+    """The video configuration's shape (12 heads, 512 tiles of 64, the last of 56),
+    32 tiles kept per query tile: every list of every head, bit for bit."""
+    w = gen.video()
+    print("coarse video full size", flush=True)
+    check(w.q, w.k, w.v, w.vbs, w.T, 32, label="video")
+
+
+def test_layer_output_coarse_then_fine_then_combine():
+    """The whole layer on the ragged configuration: the coarse stage picks 16 key tiles
+    per query tile, the fine forward attends to them, and the gated coarse output is
+    added: out = fine + gate * coarse (the oracle chain of the same three steps)."""
+    import torch
+
+    import oracle
+
+    w = gen.ragged(gate=True)
+    (gate_bits,) = oracle.tile_layout([w.tok["gate"]], w.tile_src_token, w.T)
+    q, k, v, gate = (to_dev(x) for x in (w.q, w.k, w.v, gate_bits))
+    vbs = to_dev(w.vbs)
+    idx, num, oc = bsa.coarse(q, k, v, vbs, w.T, 16)
+    out = bsa.fwd(q, k, v, idx, num, vbs, w.T)
+    bsa.coarse_combine(out, gate, oc, vbs, w.T)
+    torch.cuda.synchronize()
+    ref_idx, ref_num, ref_oc = oracle.coarse(w.q, w.k, w.v, w.vbs, w.T, 16)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref_idx)
+    fine = oracle.fwd(w.q, w.k, w.v, ref_idx, ref_num, w.vbs, w.T)
+    g = gen.bf16_bits_to_f32(gate_bits)
+    valid = (np.arange(w.S) % w.T) < np.repeat(w.vbs, w.T)
+    want = fine + np.where(valid[None, None, :, None], g * np.repeat(ref_oc, w.T, axis=2), 0.0)
+    compare(bits_from_dev(out), want.astype(np.float32), label="layer output")
+
+
+def test_graph_capture_of_the_coarse_stage():
+    """The four coarse launches captured into a graph replay the eager lists bit for bit."""
+    import torch
+
+    rng = np.random.default_rng(11)
+    T, D, NT = 128, 128, 20
+    vbs = np.full(NT, T, np.int32)
+    q, k, v = (to_dev(randn(rng, (1, 4, NT * T, D))) for _ in range(3))
+    dvbs = to_dev(vbs)
+    ws = torch.empty(bsa.coarse_workspace_size(1, 4, NT, T, D), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((1, 4, NT, 6), dtype=torch.int32, device="cuda")
+    num = torch.empty((1, 4, NT), dtype=torch.int32, device="cuda")
+    oc = torch.empty((1, 4, NT, D), dtype=torch.float32, device="cuda")
+    bsa.coarse(q, k, v, dvbs, T, 6, q2k_idx=idx, q2k_num=num, coarse_out=oc, workspace=ws)
+    torch.cuda.synchronize()
+    eager = (idx.cpu().numpy(), num.cpu().numpy(), oc.cpu().numpy())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        bsa.coarse(q, k, v, dvbs, T, 6, q2k_idx=idx, q2k_num=num, coarse_out=oc, workspace=ws)
+    for r in range(3):
+        idx.fill_(-7)
+        oc.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(idx.cpu().numpy(), eager[0], err_msg=f"replay {r}")
+        np.testing.assert_array_equal(num.cpu().numpy(), eager[1])
+        np.testing.assert_array_equal(oc.cpu().numpy(), eager[2])
