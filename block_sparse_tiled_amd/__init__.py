@@ -13,6 +13,7 @@ from .api import (  # noqa: F401
     cube_tile_map,
     fwd,
     fwd_lse,
+    fwd_noalloc,
     fwd_out_shape,
     load,
     status_string,

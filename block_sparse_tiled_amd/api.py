@@ -29,6 +29,7 @@ STATUS = {
     4: "BSA_ERR_NO_DEVICE",
     5: "BSA_ERR_UNSUPPORTED_DEVICE",
     6: "BSA_ERR_HIP",
+    7: "BSA_ERR_SCRATCH_LIMIT",
 }
 
 
@@ -56,6 +57,8 @@ def load():
     lib.bsa_within_launch_limits.restype = ctypes.c_int
     lib.bsa_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, i64, i64, i64, i32, i32, vp, i64, vp]
     lib.bsa_fwd.restype = ctypes.c_int
+    lib.bsa_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, i64, i64, i64, i32, i32, vp]
+    lib.bsa_fwd_noalloc.restype = ctypes.c_int
     lib.bsa_fwd_workspace_size.argtypes = [i64, i64, i64, i32, i32, i32, ctypes.POINTER(i64)]
     lib.bsa_fwd_workspace_size.restype = ctypes.c_int
     lib.bsa_tile_layout.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp, i32,
@@ -199,6 +202,24 @@ def fwd(q, k, v, q2k_idx, q2k_num, block_sizes, tile, out=None, workspace="auto"
         _check(lib.bsa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(q2k_idx), _ptr(q2k_num),
                            _ptr(block_sizes), tile, _ptr(out), B, H, NT, D, MS, ws_ptr, ws_bytes,
                            _stream_handle(device)))
+    return out
+
+
+def fwd_noalloc(q, k, v, q2k_idx, q2k_num, block_sizes, tile, out):
+    """``fwd`` through bsa_fwd_noalloc: no device memory is allocated (the library's
+    fixed per-GPU scratch array holds the split workspace; calls that overlap on one GPU
+    race on it).  ``out`` must be given."""
+    import torch
+
+    lib = load()
+    device, B, H, S, D, NT = _fwd_args(q, k, v, q2k_idx, q2k_num, block_sizes, tile)
+    _require(out, "out", torch.bfloat16, device, 4)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    with torch.cuda.device(device):
+        _check(lib.bsa_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(q2k_idx), _ptr(q2k_num),
+                                   _ptr(block_sizes), tile, _ptr(out), B, H, NT, D,
+                                   int(q2k_idx.shape[3]), _stream_handle(device)))
     return out
 
 
