@@ -35,6 +35,7 @@ WORKLOAD_NAMES = {
     "video": "video_sparse_64tile",
     "stress": "stress_ragged_naninf",
     "dense25": "dense_shape_25pct",
+    "dense256": "dense_limit_31200_tile256",
     "tiny": "tiny",
 }
 KERNEL_SOURCES = ["bsa_fwd_common.h", "bsa_fwd.hip"]
@@ -247,6 +248,65 @@ def run_backward(args, w, flops_fwd, put, dev):
     print(json.dumps(rec), flush=True)
 
 
+def run_coarse(args, w, put, dev):
+    """The coarse stage (bsa_coarse: pooling, coarse logits, top-k selection, coarse output)
+    on the workload's tiled Q, K, V, keeping as many tiles per query tile as the workload's
+    lists hold.  Prints its own JSON line.  The roofline kernel is the pooling, which reads
+    every valid row of Q, K and V once (HBM-bound); its algorithmic bytes are divided by the
+    whole stage's time (four launches), a lower bound on that kernel's own rate."""
+    import torch
+
+    import block_sparse_tiled_amd as bsa
+
+    q, k, v, vbs = put(w.q), put(w.k), put(w.v), put(w.vbs)
+    topk = int(w.MS)
+    idx = torch.empty((w.B, w.H, w.NT, topk), dtype=torch.int32, device=dev)
+    num = torch.empty((w.B, w.H, w.NT), dtype=torch.int32, device=dev)
+    oc = torch.empty((w.B, w.H, w.NT, w.D), dtype=torch.float32, device=dev)
+    ws = torch.empty(bsa.coarse_workspace_size(w.B, w.H, w.NT, w.T, w.D), dtype=torch.uint8,
+                     device=dev)
+
+    def call():
+        bsa.coarse(q, k, v, vbs, w.T, topk, q2k_idx=idx, q2k_num=num, coarse_out=oc, workspace=ws)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record()
+        call()
+        ev[s][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    valid = int(w.vbs.sum())
+    pool_bytes = 3 * w.B * w.H * valid * w.D * 2 + 3 * w.B * w.H * w.NT * w.D * 4
+    logit_flops = 2 * w.B * w.H * w.NT * w.NT * w.D
+    rec = {
+        "metric": "coarse stage ms/call (pooling, logits, top-k selection, coarse output)",
+        "value": round(ms, 5),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": False,
+        "dtype": "f32 (bf16 inputs)",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[args.workload], "B": w.B, "H": w.H, "D": w.D,
+                   "tile": w.T, "num_tiles": w.NT, "topk": topk, "valid_tokens": valid,
+                   "pool_bytes": pool_bytes, "logit_flops": logit_flops,
+                   "step": "bsa_coarse (4 launches), inputs resident in HBM"},
+        "roofline": {"bound": "hbm", "kernel": "coarse_pool_kernel (whole stage time)",
+                     "achieved": round(pool_bytes / (ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(pool_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "traffic": None},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -264,6 +324,9 @@ def main():
     ap.add_argument("--cold", type=int, default=0,
                     help="also time this many forward calls, each after a 1 GiB scratch write "
                          "(cache-cold; off by default so that profiles count only the timed steps)")
+    ap.add_argument("--coarse", action="store_true",
+                    help="time the coarse stage (tile selection and coarse output) instead "
+                         "(prints its own JSON line)")
     ap.add_argument("--fwd-only", action="store_true",
                     help="time only the attention launch (the tile buffers are laid out once "
                          "before timing) -- for profiling")
@@ -300,6 +363,9 @@ def main():
 
     if args.backward:
         run_backward(args, w, flops, put, dev)
+        return
+    if args.coarse:
+        run_coarse(args, w, put, dev)
         return
 
     tok = [put(w.tok[x]) for x in ("q", "k", "v", "gate")]

@@ -17,8 +17,8 @@
 //   - the layer output is the fine output plus the gate times the coarse
 //     output of the token's tile.
 // The pooled means and the logits are binary32 in a fixed order (rows summed
-// in order then one division; products and sums over d ascending, never
-// fused), so the selection is a fixed function of the inputs, reproducible
+// in order then one division; one fused multiply-add per term over d
+// ascending), so the selection is a fixed function of the inputs, reproducible
 // bit for bit by a plain CPU loop.
 //
 // Kernels (all memory- or latency-bound; the stage is small next to the fine
@@ -26,13 +26,14 @@
 //   - coarse_pool_kernel: one thread per (tensor, head, tile, 16-byte chunk
 //     of a row), summing the tile's valid rows in order (8 columns each);
 //   - coarse_logits_kernel: the NT x NT logits per head, 64 x 64 per
-//     workgroup, each thread 4 x 4 of them, d ascending through LDS;
+//     workgroup, each thread a 4 x 4 block of them, d ascending through LDS,
+//     one fused multiply-add per term;
 //   - coarse_select_kernel: one wave per query tile; the row's keys in
 //     registers, the k-th largest found by a 32-step bisection on their
 //     order-preserving integer images (one ballot count per step), then the
 //     kept tiles written in ascending order through ballot prefix counts;
 //     also turns the row into softmax weights for the coarse output;
-//   - coarse_out_kernel: those weights times the pooled values;
+//   - coarse_out_kernel: those weights times the pooled values, on fp32 MFMA;
 //   - coarse_combine_kernel: out += gate * coarse output, valid rows only.
 #include <hip/hip_runtime.h>
 
@@ -79,17 +80,19 @@ __global__ __launch_bounds__(256) void coarse_pool_kernel(
   }
 }
 
-// ---- logits: g[bh][i][j] = sum_d qm[bh][i][d] * km[bh][j][d], d ascending, no fusing --------
-// 64 x 64 logits per workgroup of 256 threads; thread (ty, tx) owns rows ty + 16a and
-// columns tx + 16b (a, b < 4).  The pooled rows pass through LDS 32 columns of d at a
-// time, transposed (d-major) so that a thread's four rows (columns) are 16 apart.
+// ---- logits: g[bh][i][j] = sum_d qm[bh][i][d] * km[bh][j][d], d ascending, one fused -------
+// ---- multiply-add per term (a single rounding each, as C's fmaf) ------------------------
+// 64 x 64 logits per workgroup of 256 threads; thread (ty, tx) owns the 4 x 4 block of
+// rows 4 ty .. 4 ty + 3 and columns 4 tx .. 4 tx + 3, each logit summed by that one
+// thread over d ascending.  The pooled rows pass through LDS 32 columns of d at a time,
+// transposed (d-major), so that a thread's four rows (columns) are one 16-byte read.
 template <int D>
 __global__ __launch_bounds__(256) void coarse_logits_kernel(const float* __restrict__ qm,
                                                             const float* __restrict__ km,
                                                             int num_tiles,
                                                             float* __restrict__ logits) {
-  __shared__ float qs[32][65];
-  __shared__ float ks[32][65];
+  __shared__ __attribute__((aligned(16))) float qs[32][68];
+  __shared__ __attribute__((aligned(16))) float ks[32][68];
   const int bh = blockIdx.z;
   const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
@@ -113,26 +116,24 @@ __global__ __launch_bounds__(256) void coarse_logits_kernel(const float* __restr
     __syncthreads();
 #pragma unroll 4
     for (int dd = 0; dd < 32; ++dd) {
-      float qa[4], kb[4];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) qa[a] = qs[dd][ty + 16 * a];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) kb[b] = ks[dd][tx + 16 * b];
+      const float4 qa = *reinterpret_cast<const float4*>(&qs[dd][4 * ty]);
+      const float4 kb = *reinterpret_cast<const float4*>(&ks[dd][4 * tx]);
+      const float qv[4] = {qa.x, qa.y, qa.z, qa.w}, kv[4] = {kb.x, kb.y, kb.z, kb.w};
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = __fadd_rn(acc[a][b], __fmul_rn(qa[a], kb[b]));
+        for (int b = 0; b < 4; ++b) acc[a][b] = __fmaf_rn(qv[a], kv[b], acc[a][b]);
     }
     __syncthreads();
   }
   float* out = logits + static_cast<int64_t>(bh) * num_tiles * num_tiles;
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
-    const int i = i0 + ty + 16 * a;
+    const int i = i0 + 4 * ty + a;
     if (i >= num_tiles) continue;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      const int j = j0 + tx + 16 * b;
+      const int j = j0 + 4 * tx + b;
       if (j < num_tiles) out[static_cast<int64_t>(i) * num_tiles + j] = acc[a][b];
     }
   }
@@ -241,57 +242,57 @@ __global__ __launch_bounds__(256) void coarse_select_kernel(
 }
 
 // ---- coarse output: oc[bh][i][:] = sum_j w[bh][i][j] * vm[bh][j][:] -----------------------
-// 64 query tiles x 64 columns per workgroup (thread: 4 x 4), j through LDS 32 at a time.
+// fp32 MFMA (v_mfma_f32_32x32x2_f32): a workgroup of 4 waves per 32 query tiles x 32
+// columns, each wave a quarter of the key-tile range, the four partial blocks added in
+// LDS.  Lane l feeds A[l % 32][l / 32] = w[i0 + l % 32][j] and B[l / 32][l % 32] =
+// vm[j][c0 + l % 32] with j = jq + (l / 32) * half + step for the wave's quarter
+// starting at jq: the two halves of the quarter run side by side in the instruction's
+// two k slots, and each lane reads its weights row contiguously.  C (32 x 32): lane l,
+// register r holds C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].  The order of the sum is
+// free here (the output is compared within a tolerance); the logits, which decide the
+// lists, are formed apart in a fixed order.
 template <int D>
 __global__ __launch_bounds__(256) void coarse_out_kernel(const float* __restrict__ w,
                                                          const float* __restrict__ vm,
                                                          int num_tiles, float* __restrict__ oc) {
-  __shared__ float ws[32][65];
-  __shared__ float vs[32][65];
+  __shared__ float part[3][16][64];
   const int bh = blockIdx.z;
-  const int i0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-  const float* wh = w + static_cast<int64_t>(bh) * num_tiles * num_tiles;
-  const float* vh = vm + static_cast<int64_t>(bh) * num_tiles * D;
-  float acc[4][4];
+  const int i0 = blockIdx.x * 32, c0 = blockIdx.y * 32;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 31, h = lane >> 5;
+  const int quarter = (num_tiles + 3) >> 2;
+  const int jq0 = wave * quarter;
+  const int jq1 = jq0 + quarter < num_tiles ? jq0 + quarter : num_tiles;
+  const int half_len = (quarter + 1) >> 1;
+  const int jb = jq0 + h * half_len;
+  const int i = i0 + r;
+  const float* wrow = w + (static_cast<int64_t>(bh) * num_tiles + (i < num_tiles ? i : 0)) * num_tiles;
+  const float* vh = vm + static_cast<int64_t>(bh) * num_tiles * D + c0 + r;
+  f32x16_t acc = {};
+  constexpr int kU = 8;
+  for (int s0 = 0; s0 < half_len; s0 += kU) {
+    float a[kU], b[kU];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0f;
-  for (int j0 = 0; j0 < num_tiles; j0 += 32) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int idx = tid + 256 * e;
-      const int row = idx >> 5, jj = idx & 31;  // weights: row i0 + row, column j0 + jj
-      const int i = i0 + row, j = j0 + jj;
-      ws[jj][row] = (i < num_tiles && j < num_tiles) ? wh[static_cast<int64_t>(i) * num_tiles + j]
-                                                     : 0.0f;
-      const int vr = idx >> 6, vc = idx & 63;  // values: row j0 + vr, column c0 + vc
-      const int jv = j0 + vr;
-      if (vr < 32) vs[vr][vc] = jv < num_tiles ? vh[static_cast<int64_t>(jv) * D + c0 + vc] : 0.0f;
+    for (int u = 0; u < kU; ++u) {
+      const int step = s0 + u, j = jb + step;
+      const bool ok = step < half_len && j < jq1;
+      a[u] = ok && i < num_tiles ? wrow[j] : 0.0f;
+      b[u] = ok ? vh[static_cast<int64_t>(j) * D] : 0.0f;
     }
-    __syncthreads();
-#pragma unroll 4
-    for (int jj = 0; jj < 32; ++jj) {
-      float wa[4], vb[4];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) wa[a] = ws[jj][ty + 16 * a];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) vb[b] = vs[jj][tx + 16 * b];
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] += wa[a] * vb[b];
-    }
-    __syncthreads();
+    for (int u = 0; u < kU; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[u], b[u], acc, 0, 0, 0);
   }
+  if (wave > 0) {
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int i = i0 + ty + 16 * a;
-    if (i >= num_tiles) continue;
+    for (int g = 0; g < 16; ++g) part[wave - 1][g][lane] = acc[g];
+  }
+  __syncthreads();
+  if (wave != 0) return;
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
-      oc[(static_cast<int64_t>(bh) * num_tiles + i) * D + c0 + tx + 16 * b] = acc[a][b];
+  for (int g = 0; g < 16; ++g) {
+    const float v = acc[g] + part[0][g][lane] + part[1][g][lane] + part[2][g][lane];
+    const int row = i0 + 8 * (g >> 2) + 4 * h + (g & 3);
+    if (row < num_tiles) oc[(static_cast<int64_t>(bh) * num_tiles + row) * D + c0 + r] = v;
   }
 }
 
@@ -362,6 +363,10 @@ hipError_t launch_coarse_d(const bsa::CoarseProblem& p, hipStream_t stream) {
     hipLaunchKernelGGL(coarse_select_kernel<4>, sgrid, dim3(256), 0, stream, logits,
                        p.block_sizes, p.num_tiles, tiles_all, p.topk, p.max_sel, scale, p.q2k_idx,
                        p.q2k_num, weights);
+  else if (p.num_tiles <= 512)
+    hipLaunchKernelGGL(coarse_select_kernel<8>, sgrid, dim3(256), 0, stream, logits,
+                       p.block_sizes, p.num_tiles, tiles_all, p.topk, p.max_sel, scale, p.q2k_idx,
+                       p.q2k_num, weights);
   else if (p.num_tiles <= 1024)
     hipLaunchKernelGGL(coarse_select_kernel<16>, sgrid, dim3(256), 0, stream, logits,
                        p.block_sizes, p.num_tiles, tiles_all, p.topk, p.max_sel, scale, p.q2k_idx,
@@ -373,8 +378,9 @@ hipError_t launch_coarse_d(const bsa::CoarseProblem& p, hipStream_t stream) {
   err = hipGetLastError();
   if (err != hipSuccess || !weights) return err;
   hipLaunchKernelGGL(coarse_out_kernel<D>,
-                     dim3(D / 64, nb, static_cast<unsigned>(p.batch_heads)), dim3(256), 0, stream,
-                     logits, vm, p.num_tiles, p.coarse_out);
+                     dim3(static_cast<unsigned>((p.num_tiles + 31) / 32), D / 32,
+                          static_cast<unsigned>(p.batch_heads)),
+                     dim3(256), 0, stream, logits, vm, p.num_tiles, p.coarse_out);
   return hipGetLastError();
 }
 

@@ -276,6 +276,17 @@ def dense(seed=3, gate=False, density_tiles=None, name="dense"):
                  pick, rng, MS=n, gate=gate)
 
 
+def dense256(seed=6, gate=False):
+    """The dense shape in 256-token tiles: B=1, H=6, D=128, 31200 tokens in 122 tiles of 256
+    (last 224); every list holds every tile in order."""
+    rng = np.random.default_rng(seed)
+    B, H, NT, T = 1, 6, 122, 256
+    vbs = np.full(NT, T, np.int32)
+    vbs[-1] = 31200 - T * (NT - 1)
+    return build("dense256", B, H, 128, T, vbs, lambda rng: np.full((B, H, NT), NT, np.int32),
+                 lambda rng, b, h, i, n: np.arange(NT), rng, MS=NT, gate=gate)
+
+
 def dense25(seed=5, gate=False):
     """The dense shape at 25 % tile density: 61 random tiles of 244 per list."""
     return dense(seed, gate, density_tiles=61, name="dense25")
@@ -318,6 +329,7 @@ CONFIGS = {
     "dense": dense,
     "stress": stress,
     "dense25": dense25,
+    "dense256": dense256,
 }
 
 

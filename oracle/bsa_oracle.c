@@ -261,8 +261,8 @@ float oracle_softmax_scale(int64_t D) { return (float)(1.0 / sqrt((double)D)); }
  *   pooling   every tile t with vbs[t] > 0 becomes one token, the mean of its
  *             valid rows: xm[t][d] = (sum over s < vbs[t], ascending, of
  *             x[t*T + s][d]) / vbs[t], binary32 sums and one division;
- *   logits    g[i][j] = sum over d ascending of qm[i][d] * km[j][d], binary32
- *             products and sums (no fused multiply-add);
+ *   logits    g[i][j] = sum over d ascending of qm[i][d] * km[j][d], one fused
+ *             multiply-add per term (fmaf: the product and the sum rounded once);
  *   selection for a query tile i with vbs[i] > 0, the candidates are the key
  *             tiles j with vbs[j] > 0, ranked by g[i][j] descending (a NaN
  *             logit ranks as -inf, -0 as +0), equal logits by ascending j; the
@@ -274,8 +274,8 @@ float oracle_softmax_scale(int64_t D) { return (float)(1.0 / sqrt((double)D)); }
  *             l = sum p_j, divided only when l != 0 (as the fine stage);
  *             0 for a query tile with vbs[i] = 0 or without candidates.
  *
- * Everything is binary32 with contraction off, so the lists are a fixed
- * function of the inputs.
+ * Everything is binary32 with contraction off (the one fused step is the
+ * explicit fmaf), so the lists are a fixed function of the inputs.
  */
 
 /* xm [B*H, NT, D]: the mean of each tile's valid rows (0 for empty tiles). */
@@ -354,8 +354,7 @@ int oracle_coarse_select(const float *qm, const float *km, const float *vm, cons
         keep[j] = 0;
         if (vbs[j] <= 0) continue;
         float dot = 0.0f;
-        for (d = 0; d < D; ++d)
-          dot = dot + qm[(bh * NT + i) * D + d] * km[(bh * NT + j) * D + d];
+        for (d = 0; d < D; ++d) dot = fmaf(qm[(bh * NT + i) * D + d], km[(bh * NT + j) * D + d], dot);
         g[j] = dot;
         order[cand].key = rank_key(dot);
         order[cand].j = j;
