@@ -490,12 +490,14 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   if (tid == 0) slot[S::kAny] = any_keys ? 1.0f : 0.0f;
 }
 
-// Merge of the split items: one workgroup per item, the same T/32 waves and
-// lane layout as the segments that wrote the item's `splits` slots.  The
-// partials are combined in segment order with the guarded rescaling of the
-// online update (an exponent offset of 0 while the running max is -inf), so
-// the result is a fixed function of the slots; then the rows are stored as
-// for a whole item.
+// Merge of the split items: one workgroup per (item, 32-column block of the
+// output), the same T/32 waves and lane layout as the segments that wrote the
+// item's `splits` slots (at most 4).  Every slot's values for the block are
+// loaded first; then the partials are combined in segment order with the
+// guarded rescaling of the online update (an exponent offset of 0 while the
+// running max is -inf), so the result is a fixed function of the slots, and
+// the block's rows are stored as for a whole item (the first block's
+// workgroup also writes the log-sum-exp).
 template <int T, int D>
 __global__ __launch_bounds__(2 * T) void bsa_fwd_merge_kernel(
     const float* __restrict__ ws, const int32_t* __restrict__ vbs, uint16_t* __restrict__ out,
@@ -503,46 +505,88 @@ __global__ __launch_bounds__(2 * T) void bsa_fwd_merge_kernel(
     uint16_t* __restrict__ out_lo, int sub_shift) {
   using C = Cfg<T, D>;
   using S = Slot<T, D>;
+  constexpr int kMaxSplits = 4;
   const int m = blockIdx.x;
+  const int db = blockIdx.y;
   const int item = n_whole + m;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = launder(lane);
-  f32x16_t acc[C::kDBlocks];
+  float4 xv[kMaxSplits][4];
+  float ms[kMaxSplits], ls[kMaxSplits], as[kMaxSplits];
 #pragma unroll
-  for (int db = 0; db < C::kDBlocks; ++db)
+  for (int sg = 0; sg < kMaxSplits; ++sg) {
+    if (sg >= splits) break;
+    const float* slot = ws + (static_cast<int64_t>(m) * splits + sg) * S::kFloats;
+    ms[sg] = slot[S::kM + wave * 64 + ln];
+    ls[sg] = slot[S::kL + wave * 64 + ln];
+    as[sg] = slot[S::kAny];
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) acc[db][rr] = 0.0f;
+    for (int r4 = 0; r4 < 4; ++r4)
+      xv[sg][r4] = *reinterpret_cast<const float4*>(
+          slot + (((wave * C::kDBlocks + db) * 4 + r4) * 64 + ln) * 4);
+  }
+  float acc[16];
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) acc[rr] = 0.0f;
   float mm = -INFINITY, l_run = 0.0f;
   bool any_all = false;
-  for (int sg = 0; sg < splits; ++sg) {
-    const float* slot = ws + (static_cast<int64_t>(m) * splits + sg) * S::kFloats;
-    const float ms = slot[S::kM + wave * 64 + ln];
-    const float ls = slot[S::kL + wave * 64 + ln];
-    const float as = slot[S::kAny];
-    const float mn = fmaxf(mm, ms);
+#pragma unroll
+  for (int sg = 0; sg < kMaxSplits; ++sg) {
+    if (sg >= splits) break;
+    const float mn = fmaxf(mm, ms[sg]);
     const float mnc = (mn == -INFINITY ? 0.0f : mn) * c;
     const float sa = __builtin_amdgcn_exp2f(mm * c - mnc);
-    const float sb = __builtin_amdgcn_exp2f(ms * c - mnc);
+    const float sb = __builtin_amdgcn_exp2f(ms[sg] * c - mnc);
     mm = mn;
-    l_run = l_run * sa + ls * sb;
-    any_all = any_all || as != 0.0f;
+    l_run = l_run * sa + ls[sg] * sb;
+    any_all = any_all || as[sg] != 0.0f;
 #pragma unroll
-    for (int db = 0; db < C::kDBlocks; ++db)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const float4 xv = *reinterpret_cast<const float4*>(
-            slot + (((wave * C::kDBlocks + db) * 4 + r4) * 64 + ln) * 4);
-        acc[db][4 * r4 + 0] = acc[db][4 * r4 + 0] * sa + xv.x * sb;
-        acc[db][4 * r4 + 1] = acc[db][4 * r4 + 1] * sa + xv.y * sb;
-        acc[db][4 * r4 + 2] = acc[db][4 * r4 + 2] * sa + xv.z * sb;
-        acc[db][4 * r4 + 3] = acc[db][4 * r4 + 3] * sa + xv.w * sb;
-      }
+    for (int r4 = 0; r4 < 4; ++r4) {
+      acc[4 * r4 + 0] = acc[4 * r4 + 0] * sa + xv[sg][r4].x * sb;
+      acc[4 * r4 + 1] = acc[4 * r4 + 1] * sa + xv[sg][r4].y * sb;
+      acc[4 * r4 + 2] = acc[4 * r4 + 2] * sa + xv[sg][r4].z * sb;
+      acc[4 * r4 + 3] = acc[4 * r4 + 3] * sa + xv[sg][r4].w * sb;
+    }
   }
+  // normalise and store this block's columns of the wave's 32 rows (as store_tile_rows)
   const int64_t ibh = item / num_tiles;
-  store_tile_rows<T, D>(acc, mm, l_run, any_all, ibh, item - static_cast<int>(ibh) * num_tiles,
-                        num_tiles, vbs, sub_shift, wave, lane, c, out, lse, out_lo);
+  const int itile = item - static_cast<int>(ibh) * num_tiles;
+  const int vq = clampi(vbs[itile >> sub_shift] - T * (itile & ((1 << sub_shift) - 1)), 0, T);
+  const int row = wave * 32 + (ln & 31);
+  float l_tot;
+  {
+    float lo_half, hi_half;
+    swap_halves(l_run, lo_half, hi_half);
+    l_tot = lo_half + hi_half;
+  }
+  const bool zero_row = !any_all || row >= vq;
+  const float inv = l_tot != 0.0f ? 1.0f / l_tot : __builtin_nanf("");
+  const int64_t row_id = (ibh * num_tiles + itile) * T + row;
+  if (lse != nullptr && db == 0 && ln < 32) {
+    const float mc = (mm == -INFINITY ? 0.0f : mm) * c;
+    lse[row_id] = zero_row ? -INFINITY : (mc + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+  }
+  const int64_t off = row_id * D + 32 * db + 4 * (ln >> 5);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    float x[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = zero_row ? 0.0f : acc[4 * g + e] * inv;
+    const unsigned w0 = __builtin_bit_cast(unsigned, to_bf16x2(x[0], x[1]));
+    const unsigned w1 = __builtin_bit_cast(unsigned, to_bf16x2(x[2], x[3]));
+    *reinterpret_cast<uint2*>(out + off + 8 * g) = make_uint2(w0, w1);
+    if (lse != nullptr) {
+      const float r0 = x[0] - __uint_as_float(w0 << 16);
+      const float r1 = x[1] - __uint_as_float(w0 & 0xffff0000u);
+      const float r2 = x[2] - __uint_as_float(w1 << 16);
+      const float r3 = x[3] - __uint_as_float(w1 & 0xffff0000u);
+      *reinterpret_cast<uint2*>(out_lo + off + 8 * g) =
+          make_uint2(__builtin_bit_cast(unsigned, to_bf16x2(r0, r1)),
+                     __builtin_bit_cast(unsigned, to_bf16x2(r2, r3)));
+    }
+  }
 }
 
 template <int T, int D>
@@ -574,8 +618,8 @@ hipError_t launch(const bsa::FwdProblem& p, hipStream_t stream) {
   const void* merge = reinterpret_cast<const void*>(&bsa_fwd_merge_kernel<T, D>);
   const float* wsc = ws;
   void* margs[] = {&wsc, &vbs, &out, &nt, &n_whole, &splits, &cc, &lse, &out_lo, &sub_shift};
-  return hipLaunchKernel(merge, dim3(static_cast<unsigned>(n_split_units / splits)), block, margs,
-                         0, stream);
+  return hipLaunchKernel(merge, dim3(static_cast<unsigned>(n_split_units / splits), Cfg<T, D>::kDBlocks),
+                         block, margs, 0, stream);
 }
 
 // Work split.  Workgroups run in rounds of `resident` (occupancy x CUs); the
