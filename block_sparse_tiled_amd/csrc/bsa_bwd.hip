@@ -634,7 +634,7 @@ void dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
           load(kDkvOrder<NQB, NA, 2 * NDB>.st[p + kAhead], (p + kAhead) % kRing);
         constexpr int st = kDkvOrder<NQB, NA, 2 * NDB>.st[p];
         constexpr int qb = st / NS, k = st % NS, sl = p % kRing;
-        if (k == NA) {
+        if constexpr (k == NA) {
           // the first 16-query chunk, which the first dV/dK steps use, once S
           // and dP are complete (the MFMAs issued since their last step run
           // beside it)
@@ -644,7 +644,7 @@ void dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
           sb[0] = pack8(dp, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
-        if (k < NA) {
+        if constexpr (k < NA) {
           s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[sl], kop[k], k ? s : zero16, 0, 0, 0);
           dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rb[sl], vop[k], k ? dp : zero16, 0, 0, 0);
         } else {
@@ -654,10 +654,10 @@ void dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         }
         __builtin_amdgcn_sched_barrier(0);
         // the second chunk under the MFMAs of the first two dV/dK steps
-        if (k == NA) {
+        if constexpr (k == NA) {
           softmax_group(qb, 2);
           __builtin_amdgcn_sched_barrier(0);
-        } else if (k == NA + 1) {
+        } else if constexpr (k == NA + 1) {
           softmax_group(qb, 3);
           pb[1] = pack8(s, 8);
           sb[1] = pack8(dp, 8);
