@@ -152,3 +152,38 @@ def test_graph_capture_of_the_coarse_stage():
         np.testing.assert_array_equal(idx.cpu().numpy(), eager[0], err_msg=f"replay {r}")
         np.testing.assert_array_equal(num.cpu().numpy(), eager[1])
         np.testing.assert_array_equal(oc.cpu().numpy(), eager[2])
+
+
+def draw_coarse_problem(case):
+    """A seeded random coarse-stage problem: tile 64/128/256, head size 64/128, up to 700
+    tiles with empty and short ones, topk anywhere from 0 to past the tile count, and (in
+    a third of the cases) inputs from a handful of values, so that equal logits are
+    common and the lower-index rule decides."""
+    rng = np.random.default_rng(9000 + case)
+    T = int(rng.choice([64, 128, 256]))
+    D = int(rng.choice([64, 128]))
+    NT = int(rng.choice([1, 2, 5, 17, 64, 130, 300, 700]))
+    B, H = (1, 1) if NT > 200 else (int(rng.integers(1, 3)), int(rng.integers(1, 4)))
+    vbs = rng.integers(0, T + 1, NT).astype(np.int32)
+    vbs[rng.random(NT) < 0.2] = 0
+    vbs[rng.random(NT) < 0.3] = T
+    topk = int(rng.integers(0, NT + 3))
+    max_sel = topk + int(rng.integers(0, 3))
+    ties = rng.random() < 0.35
+    shape = (B, H, NT * T, D)
+    if ties:
+        vals = np.array([-1.0, -0.5, 0.0, 0.5, 1.0], np.float32)
+        q, k, v = (gen.to_bf16_bits(vals[rng.integers(0, 5, shape)]) for _ in range(3))
+    else:
+        q, k, v = (randn(rng, shape, float(rng.choice([0.5, 1.0, 2.0]))) for _ in range(3))
+    pad = (np.arange(NT * T) % T) >= np.repeat(vbs, T)
+    for x in (q, k, v):
+        x[:, :, pad] = rng.choice([0x7FC0, 0x7F80, 0xFF80, 0])
+    return q, k, v, vbs, T, topk, max_sel, f"T={T} D={D} B={B} H={H} NT={NT} topk={topk} ties={ties}"
+
+
+@pytest.mark.parametrize("case", range(40))
+def test_coarse_sweep(case):
+    q, k, v, vbs, T, topk, max_sel, desc = draw_coarse_problem(case)
+    print(f"coarse sweep {case}: {desc}", flush=True)
+    check(q, k, v, vbs, T, topk, max_sel=max_sel, label=desc)
