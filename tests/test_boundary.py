@@ -275,3 +275,67 @@ def test_overflowing_batch_times_heads_is_refused_not_a_crash():
     code = _HUGE_SIZES.format(root=ROOT, big=1 << 32)
     res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
     assert res.returncode == 0, f"rc {res.returncode}: {res.stdout} {res.stderr[-2000:]}"
+
+
+def coarse_call(lib, topk=2, max_sel=2, NT=4, tile=64, D=64, B=1, H=1, ws=None, ws_bytes=1 << 20,
+                outs=None, ins=None):
+    """bsa_coarse with fake pointers: inputs q, k, v, block_sizes = 0..3, outputs
+    q2k_idx, q2k_num, coarse_out = 4..6, workspace 7."""
+    i = [fake(n) for n in range(4)] if ins is None else ins
+    o = [fake(4 + n) for n in range(3)] if outs is None else outs
+    w = fake(7) if ws is None else ws
+    return lib.bsa_coarse(i[0], i[1], i[2], i[3], tile, topk, o[0], o[1], o[2], B, H, NT, D,
+                          max_sel, w, ws_bytes, NUL)
+
+
+def test_coarse_rejects_bad_arguments(lib):
+    expected = {OK, NO_DEVICE, UNSUPPORTED}
+    assert coarse_call(lib, topk=-1) == INVALID
+    assert coarse_call(lib, topk=3, max_sel=2) == INVALID  # the lists cannot hold topk tiles
+    assert coarse_call(lib, B=-1) == INVALID
+    assert coarse_call(lib, tile=96) == SHAPE
+    assert coarse_call(lib, D=32) == SHAPE
+    assert coarse_call(lib, NT=4097) == SHAPE  # more tiles than the selection holds
+    assert coarse_call(lib, H=65536) == LIMITS
+    assert coarse_call(lib, ws=NUL) == INVALID  # the workspace is required
+    need = ctypes.c_int64(0)
+    assert lib.bsa_coarse_workspace_size(1, 1, 4, 64, 64, ctypes.byref(need)) == OK
+    assert need.value == 4 * 1 * 4 * (3 * 64 + 4)
+    assert coarse_call(lib, ws_bytes=need.value - 4) == INVALID  # too small
+    assert coarse_call(lib, ws_bytes=need.value) in expected
+    # outputs overlapping an input, each other or the workspace
+    o = [fake(4 + n) for n in range(3)]
+    assert coarse_call(lib, outs=[fake(0), o[1], o[2]]) == INVALID
+    assert coarse_call(lib, outs=[o[0], o[0], o[2]]) == INVALID
+    assert coarse_call(lib, ws=fake(6)) == INVALID
+    # the coarse output is optional; an empty problem is accepted with null pointers
+    assert coarse_call(lib, outs=[o[0], o[1], NUL]) in expected
+    assert coarse_call(lib, B=0, ins=[NUL] * 4, outs=[NUL] * 3, ws=NUL, ws_bytes=0) == OK
+    assert lib.bsa_coarse_workspace_size(1, 1, 4097, 64, 64, ctypes.byref(need)) == SHAPE
+    assert lib.bsa_coarse_workspace_size(1, 1, 4, 64, 64, None) == INVALID
+
+
+def test_coarse_combine_rejects_bad_arguments(lib):
+    expected = {OK, NO_DEVICE, UNSUPPORTED}
+    call = lambda out=fake(0), gate=fake(1), oc=fake(2), bs=fake(3), tile=64, D=64: (  # noqa: E731
+        lib.bsa_coarse_combine(out, gate, oc, bs, tile, 1, 2, 4, D, NUL))
+    assert call(tile=32) == SHAPE
+    assert call(D=96) == SHAPE
+    assert call(gate=NUL) == INVALID
+    assert call(out=fake(1)) == INVALID  # out is the gate
+    assert call(oc=ctypes.c_void_p(fake(0).value + 64)) == INVALID  # coarse output inside out
+    assert call() in expected
+
+
+def test_noalloc_validates_like_fwd(lib):
+    expected = {OK, NO_DEVICE, UNSUPPORTED}
+    q = fake(0)
+    f = lambda tile=128, B=1, out=fake(6), MS=2: lib.bsa_fwd_noalloc(  # noqa: E731
+        q, fake(1), fake(2), fake(5), fake(3), fake(4), tile, out, B, 1, 2, 128, MS, NUL)
+    assert f(tile=96) == SHAPE
+    assert f(B=-1) == INVALID
+    assert f(MS=-1) == INVALID
+    assert f(out=q) == INVALID
+    assert f(B=0) == OK
+    assert f() in expected
+    assert bsa.status_string(7) != "unknown status"
