@@ -419,68 +419,144 @@ void dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 }
 
 // ---- dK, dV -------------------------------------------------------------------------------
-// Issue order of the dK/dV steps of one query tile.  Step qb*(NA+NB) + k is
-// step k of 32-query block qb: S/dP steps (k < NA), then dV/dK steps.  Once
-// a block's P and dS are complete (after its second dV/dK step) its S and dP
-// registers are free, so the next block's S/dP steps are interleaved with
-// the block's remaining dV/dK steps, the last two of which come after them:
-// the next block's softmax then runs beside those two steps' MFMAs.
-template <int NQB, int NA, int NB>
-struct DkvOrder;
-template <int NQB, int NA, int NB>
-inline constexpr DkvOrder<NQB, NA, NB> kDkvOrder{};
-template <int NQB, int NA, int NB>
-struct DkvOrder {
-  int st[NQB * (NA + NB)];
-  constexpr DkvOrder() : st{} {
-    const int tail = NB - 2 < 2 ? NB - 2 : 2;  // dV/dK steps after the next block's S/dP
-    const int mid = NB - 2 - tail;             // dV/dK steps spread among them
+// Issue schedule of the dK/dV products of one query tile.  Step qb*(NA+NB) + k
+// is step k of 32-query block qb: S/dP steps (k < NA), then dV/dK steps, the
+// first NB/2 on the block's first 16-query chunk.  A block's softmax runs in
+// four groups of four queries; P and dS of its first chunk are packed after
+// group 1, those of the second after group 3.  S/dP and the packed P/dS
+// live in kSets register sets, block qb in set qb % kSets.
+//   st[p]: the p-th step issued;
+//   sm[p]: softmax groups run after step p: 16 * block + mask of groups, or -1.
+// Two sets (one wave per SIMD at D = 128, registers to spare): block 0's S/dP
+// steps, then block 1's with block 0's groups among them; then period b runs
+// block b's dV/dK steps alternating with block b+2's S/dP steps, with block
+// b+1's groups among them.  Nothing a period's softmax touches is touched by
+// that period's products, so the exponentials run beside the matrix products.
+// One set (two waves per SIMD at D = 64, where a second set would spill): a
+// block's groups 0 and 1 after its last S/dP step, groups 2 and 3 after its
+// first two dV/dK steps; the next block's S/dP steps then go between its
+// remaining dV/dK steps, two of which come last, beside the next block's
+// first groups.
+template <int NQB, int NA, int NB, int kSets>
+struct DkvPipe {
+  static constexpr int NS = NA + NB, N = NQB * NS;
+  int st[N];
+  int sm[N];
+  constexpr DkvPipe() : st{}, sm{} {
+    for (int i = 0; i < N; ++i) sm[i] = -1;
     int p = 0;
-    for (int a = 0; a < NA; ++a) st[p++] = a;
-    for (int qb = 0; qb < NQB; ++qb) {
-      const int base = qb * (NA + NB), next = base + NA + NB;
-      st[p++] = base + NA;
-      st[p++] = base + NA + 1;
-      int b = 2;
-      if (qb + 1 < NQB) {
-        int a = 0;
-        for (int m = 0; m < mid; ++m) {
-          st[p++] = base + NA + b++;
-          for (int x = mid ? (m + 1) * NA / mid - m * NA / mid : 0; x > 0; --x) st[p++] = next + a++;
+    auto put = [&](int at, int b, int g) {
+      sm[at] = (sm[at] < 0 ? 16 * b : sm[at]) | (1 << g);
+    };
+    if (kSets == 2) {
+      // the four groups of block b spread over the `count` steps from `first`
+      // (after steps 1, 5, 9, 13 of 16; 1, 3, 5, 7 of 8; 0, 1, 2, 3 of 4)
+      auto groups = [&](int first, int count, int b) {
+        for (int g = 0; g < 4; ++g) {
+          const int x = count - 4 + g, y = 1 + g * count / 4;
+          put(first + (x < y ? x : y), b, g);
         }
-        while (a < NA) st[p++] = next + a++;
+      };
+      for (int a = 0; a < NA; ++a) st[p++] = a;
+      {
+        const int first = p;
+        for (int a = 0; a < NA; ++a) st[p++] = NS + a;
+        groups(first, NA, 0);
       }
-      while (b < NB) st[p++] = base + NA + b++;
+      for (int b = 0; b < NQB; ++b) {
+        const int first = p;
+        const bool sdp = b + 2 < NQB;
+        int x = 0, y = 0;
+        while (x < NB || (sdp && y < NA)) {
+          if (x < NB && (!sdp || y >= NA || x * NA <= y * NB)) st[p++] = b * NS + NA + x++;
+          else st[p++] = (b + 2) * NS + y++;
+        }
+        if (b + 1 < NQB) groups(first, p - first, b + 1);
+      }
+    } else {
+      const int tail = NB - 2 < 2 ? NB - 2 : 2;  // dV/dK steps after the next block's S/dP
+      const int mid = NB - 2 - tail;             // dV/dK steps spread among them
+      for (int a = 0; a < NA; ++a) st[p++] = a;
+      put(p - 1, 0, 0);
+      put(p - 1, 0, 1);
+      for (int qb = 0; qb < NQB; ++qb) {
+        const int base = qb * NS, next = base + NS;
+        st[p++] = base + NA;
+        put(p - 1, qb, 2);
+        st[p++] = base + NA + 1;
+        put(p - 1, qb, 3);
+        int b = 2;
+        if (qb + 1 < NQB) {
+          int a = 0;
+          for (int m = 0; m < mid; ++m) {
+            st[p++] = base + NA + b++;
+            for (int x = mid ? (m + 1) * NA / mid - m * NA / mid : 0; x > 0; --x) st[p++] = next + a++;
+          }
+          while (a < NA) st[p++] = next + a++;
+        }
+        while (b < NB) st[p++] = base + NA + b++;
+        if (qb + 1 < NQB) {
+          put(p - 1, qb + 1, 0);
+          put(p - 1, qb + 1, 1);
+        }
+      }
     }
   }
 };
-// An order is valid when it is a permutation of the steps that keeps each
-// block's own steps in order, starts the next block's S/dP after this
-// block's second dV/dK step (the last reader of S and dP), and its dV/dK
-// after all of this block's (the readers of P and dS).
-template <int NQB, int NA, int NB>
-constexpr bool dkv_order_valid() {
-  constexpr int NS = NA + NB, N = NQB * NS;
-  int pos[N] = {};
-  bool seen[N] = {};
+template <int NQB, int NA, int NB, int kSets>
+inline constexpr DkvPipe<NQB, NA, NB, kSets> kDkvPipe{};
+// The data flow a schedule must respect (positions in issue order; a group at
+// position q runs after step q): every step once, each block's steps in
+// order; a block's groups in order, after its last S/dP step and before the
+// S/dP step that reuses its register set (block + kSets); its dV/dK steps on
+// chunk c after its packing group 2c + 1; the packing groups of block
+// b + kSets after block b's last dV/dK step on that chunk.
+template <int NQB, int NA, int NB, int kSets>
+constexpr bool dkv_pipe_valid() {
+  constexpr auto& s = kDkvPipe<NQB, NA, NB, kSets>;
+  constexpr int NS = NA + NB, N = NQB * NS, C2 = NB / 2;
+  int pos[N] = {}, gpos[NQB][4] = {};
+  bool seen[N] = {}, gseen[NQB][4] = {};
   for (int p = 0; p < N; ++p) {
-    const int st = kDkvOrder<NQB, NA, NB>.st[p];
+    const int st = s.st[p];
     if (st < 0 || st >= N || seen[st]) return false;
     seen[st] = true;
     pos[st] = p;
+    if (s.sm[p] >= 0) {
+      const int b = s.sm[p] / 16;
+      if (b >= NQB) return false;
+      for (int g = 0; g < 4; ++g)
+        if (s.sm[p] >> g & 1) {
+          if (gseen[b][g]) return false;
+          gseen[b][g] = true;
+          gpos[b][g] = p;
+        }
+    }
   }
-  for (int qb = 0; qb < NQB; ++qb) {
-    const int b = qb * NS;
+  for (int b = 0; b < NQB; ++b) {
+    const int base = b * NS;
+    for (int g = 0; g < 4; ++g) {
+      if (!gseen[b][g]) return false;
+      if (g && gpos[b][g] < gpos[b][g - 1]) return false;
+    }
     for (int k = 1; k < NS; ++k)
-      if (pos[b + k] < pos[b + k - 1]) return false;
-    if (qb + 1 < NQB && (pos[b + NS] < pos[b + NA + 1] || pos[b + NS + NA] < pos[b + NS - 1]))
-      return false;
+      if (pos[base + k] < pos[base + k - 1]) return false;
+    if (gpos[b][0] < pos[base + NA - 1]) return false;
+    for (int k = 0; k < NB; ++k)
+      if (pos[base + NA + k] <= gpos[b][k < C2 ? 1 : 3]) return false;
+    if (b + kSets < NQB) {
+      if (pos[base + kSets * NS] <= gpos[b][3]) return false;
+      if (gpos[b + kSets][1] < pos[base + NA + C2 - 1] ||
+          gpos[b + kSets][3] < pos[base + NA + NB - 1])
+        return false;
+    }
   }
   return true;
 }
-static_assert(dkv_order_valid<4, 8, 8>() && dkv_order_valid<4, 4, 4>() &&
-                  dkv_order_valid<2, 8, 8>() && dkv_order_valid<2, 4, 4>(),
-              "dK/dV step order");
+static_assert(dkv_pipe_valid<4, 8, 8, 2>() && dkv_pipe_valid<2, 8, 8, 2>() &&
+                  dkv_pipe_valid<4, 4, 4, 1>() && dkv_pipe_valid<2, 4, 4, 1>() &&
+                  dkv_pipe_valid<4, 8, 8, 1>() && dkv_pipe_valid<4, 4, 4, 2>(),
+              "dK/dV step schedule");
 
 // At D = 128 a wave holds its K and V operands (64 registers) and two fp32
 // accumulators (128) across the whole list: one wave per SIMD, up to 512
@@ -548,18 +624,36 @@ void dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   // buffer `buf`; its statistics go to registers (threads below T), written
   // to LDS once they have landed.
   float l_next = 0.0f, d_next = 0.0f;
-  auto issue = [&](int t, int buf) {
+  TileCopy<T, D, false> copy_q, copy_o;
+  // Statistics of entry t, and the copies' sources: `copy_q` and `copy_o`
+  // are set up to issue entry t's copies into buffer `buf`.
+  auto stage = [&](int t, int buf) {
     const int2 e = tl[t];
     const int i = __builtin_amdgcn_readfirstlane(e.x);
     const int vq = __builtin_amdgcn_readfirstlane(e.y);
     const int64_t qtile = static_cast<int64_t>(i) * T;
-    dma_tile<T, D, false, true>(qh + qtile * D, qs_all[buf], wave, dl, vq);
-    dma_tile<T, D, false, true>(oh + qtile * D, ds_all[buf], wave, dl, vq);
+    copy_q.set(qh + qtile * D, qs_all[buf], wave, vq);
+    copy_o.set(oh + qtile * D, ds_all[buf], wave, vq);
     if (tid < vq) {
       const int64_t r = (bh * num_tiles + i) * T + tid;
       l_next = lse[r];
       d_next = delta[r];
     }
+  };
+  // Copy instruction n of the staged entry: Q's for even n, dO's for odd n.
+  // With kSkip, blocks wholly past the valid rows are not copied; without,
+  // their lanes fail the range check (no memory traffic), and what they
+  // leave in LDS is zeroed with the other padding rows once the copy lands.
+  auto copy_one = [&](auto nc, auto skip) {
+    constexpr int n = decltype(nc)::value;
+    constexpr bool kSkip = decltype(skip)::value;
+    if constexpr (n % 2 == 0) copy_q.template one<n / 2, kSkip>(dl, wave);
+    else copy_o.template one<n / 2, kSkip>(dl, wave);
+  };
+  constexpr int kCopies = 2 * C::kDmaPerTile;
+  auto issue = [&](int t, int buf) {
+    stage(t, buf);
+    static_for<kCopies>([&](auto nc) { copy_one(nc, std::true_type{}); });
   };
 
   for (int base = 0; base < count; base += C::kThreads) {
@@ -586,15 +680,26 @@ void dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         zero_padding_rows<T, D>(ds_, vq, wave, lane);
       }
       lds_barrier();  // tile t visible; every wave is done with tile t - 1's buffer
-      if (t + 1 < total) issue(t + 1, buf ^ 1);
+      // Tile t + 1's copies.  At D = 128 the one wave per SIMD spreads them
+      // over tile t's products: issued as one burst they would hold it for
+      // as long as the L2 -> LDS path takes to accept them.  A wave without
+      // products to hide them under issues them at once.
+      const bool has_next = t + 1 < total;
+      constexpr bool kSpread = D == 128;
+      if (has_next) {
+        if (!kSpread || wave * 32 >= vk) issue(t + 1, buf ^ 1);
+        else stage(t + 1, buf ^ 1);
+      }
     // Per 32-query block: S = Q K^T and dP = dO V^T (steps k < NA), P and dS,
     // then dV^T += dO^T P and dK^T += Q^T dS over its two 16-query chunks
-    // (steps k >= NA), issued in the order kDkvOrder gives.  With one wave per SIMD nothing hides LDS latency but
-    // the wave's own MFMAs, so the two LDS operands of every step are read
-    // kAhead steps early, through a ring of registers, across blocks and
-    // phases.  A wave whose key rows are all padding skips the compute.
+    // (steps k >= NA), in the pipelined order kDkvPipe gives.  With one wave
+    // per SIMD nothing hides LDS latency but the wave's own MFMAs, so the two
+    // LDS operands of every step are read kAhead steps early, through a ring
+    // of registers, across blocks and phases.  A wave whose key rows are all
+    // padding skips the compute.
     if (wave * 32 < vk) {
-      constexpr int NQB = T / 32, NA = C::kKSteps, NS = NA + 2 * NDB, kSteps = NQB * NS;
+      constexpr int NQB = T / 32, NA = C::kKSteps, NB = 2 * NDB, NS = NA + NB, kSteps = NQB * NS;
+      constexpr int kSets = D == 128 ? 2 : 1;
       constexpr int kAhead = 3, kRing = kAhead + 1;
       bf16x8_t ra[kRing], rb[kRing];
       auto load = [&](int st, int sl) {
@@ -610,57 +715,63 @@ void dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       };
       static_for<kAhead>([&](auto pc) {
         constexpr int p = decltype(pc)::value;
-        load(kDkvOrder<NQB, NA, 2 * NDB>.st[p], p % kRing);
+        load(kDkvPipe<NQB, NA, NB, kSets>.st[p], p % kRing);
       });
-      f32x16_t s = zero16, dp = zero16;
-      bf16x8_t pb[2], sb[2];
+      f32x16_t s[kSets], dp[kSets];
+      bf16x8_t pb[kSets][2], sb[kSets][2];
       // P and dS of block qb, four queries (one register group) at a time:
       // register r holds query 32*qb + 8*(r/4) + 4*half + r%4
-      auto softmax_group = [&](int qb, int g) {
+      auto softmax_group = [&](int qb, int g, f32x16_t& sx, f32x16_t& dx) {
         const float4 l4 = *reinterpret_cast<const float4*>(lse_s + 32 * qb + 8 * g + 4 * half);
         const float4 d4 = *reinterpret_cast<const float4*>(dlt_s + 32 * qb + 8 * g + 4 * half);
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
-          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lv[e]));
-          s[r] = pr;                      // P
-          dp[r] = pr * (dp[r] - dv4[e]);  // dS
+          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sx[r], c, -lv[e]));
+          sx[r] = pr;                     // P
+          dx[r] = pr * (dx[r] - dv4[e]);  // dS
         }
       };
       static_for<kSteps>([&](auto pc) {
         constexpr int p = decltype(pc)::value;
         if constexpr (p + kAhead < kSteps)
-          load(kDkvOrder<NQB, NA, 2 * NDB>.st[p + kAhead], (p + kAhead) % kRing);
-        constexpr int st = kDkvOrder<NQB, NA, 2 * NDB>.st[p];
-        constexpr int qb = st / NS, k = st % NS, sl = p % kRing;
-        if constexpr (k == NA) {
-          // the first 16-query chunk, which the first dV/dK steps use, once S
-          // and dP are complete (the MFMAs issued since their last step run
-          // beside it)
-          softmax_group(qb, 0);
-          softmax_group(qb, 1);
-          pb[0] = pack8(s, 0);
-          sb[0] = pack8(dp, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+          load(kDkvPipe<NQB, NA, NB, kSets>.st[p + kAhead], (p + kAhead) % kRing);
+        constexpr int st = kDkvPipe<NQB, NA, NB, kSets>.st[p];
+        constexpr int qb = st / NS, k = st % NS, sl = p % kRing, x = qb % kSets;
         if constexpr (k < NA) {
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[sl], kop[k], k ? s : zero16, 0, 0, 0);
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rb[sl], vop[k], k ? dp : zero16, 0, 0, 0);
+          s[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[sl], kop[k], k ? s[x] : zero16, 0, 0, 0);
+          dp[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rb[sl], vop[k], k ? dp[x] : zero16, 0, 0, 0);
         } else {
-          const int cc = (k - NA) / NDB, db = (k - NA) % NDB;
-          accv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[sl], pb[cc], accv[db], 0, 0, 0);
-          acck[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rb[sl], sb[cc], acck[db], 0, 0, 0);
+          constexpr int cc = (k - NA) / NDB, db = (k - NA) % NDB;
+          accv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[sl], pb[x][cc], accv[db], 0, 0, 0);
+          acck[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rb[sl], sb[x][cc], acck[db], 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
-        // the second chunk under the MFMAs of the first two dV/dK steps
-        if constexpr (k == NA) {
-          softmax_group(qb, 2);
-          __builtin_amdgcn_sched_barrier(0);
-        } else if constexpr (k == NA + 1) {
-          softmax_group(qb, 3);
-          pb[1] = pack8(s, 8);
-          sb[1] = pack8(dp, 8);
+        // copy n of tile t + 1 after step 2 + n * kCopyEvery: spread evenly
+        // over the tile, every fourth step at most
+        constexpr int kSpan = (kSteps - 3) / (kCopies - 1);
+        constexpr int kCopyEvery = kSpan < 4 ? (kSpan > 0 ? kSpan : 1) : 4;
+        static_assert(!kSpread || 2 + (kCopies - 1) * kCopyEvery < kSteps, "every copy is issued");
+        if constexpr (kSpread && p >= 2 && (p - 2) % kCopyEvery == 0 && (p - 2) / kCopyEvery < kCopies) {
+          if (has_next) copy_one(std::integral_constant<int, (p - 2) / kCopyEvery>{}, std::false_type{});
+        }
+        constexpr int smg = kDkvPipe<NQB, NA, NB, kSets>.sm[p];
+        if constexpr (smg >= 0) {
+          constexpr int b = smg / 16, y = b % kSets;
+          static_for<4>([&](auto gc) {
+            constexpr int g = decltype(gc)::value;
+            if constexpr ((smg >> g) & 1) {
+              softmax_group(b, g, s[y], dp[y]);
+              if constexpr (g == 1) {
+                pb[y][0] = pack8(s[y], 0);
+                sb[y][0] = pack8(dp[y], 0);
+              } else if constexpr (g == 3) {
+                pb[y][1] = pack8(s[y], 8);
+                sb[y][1] = pack8(dp[y], 8);
+              }
+            }
+          });
           __builtin_amdgcn_sched_barrier(0);
         }
       });
