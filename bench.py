@@ -73,6 +73,38 @@ def load_traffic(workload):
     return rec.get("fwd_bytes_per_launch")
 
 
+def library_source_digest():
+    """sha256 (first 16 hex digits) of every library source and the header: the revision
+    of the code that was timed."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_sparse_tiled_amd", "csrc")
+    for path in sorted(os.path.join(csrc, n) for n in os.listdir(csrc)) + \
+            [os.path.join(ROOT, "include", "bsa.h")]:
+        if path.endswith((".hip", ".h")):
+            with open(path, "rb") as f:
+                h.update(os.path.basename(path).encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def clock_levels():
+    """The shader (sclk) and memory (mclk) clock levels the driver exposes, in MHz, with the
+    one current when read ("*"); None where sysfs does not show them."""
+    import glob
+
+    out = {}
+    for kind in ("sclk", "mclk"):
+        for path in sorted(glob.glob(f"/sys/class/drm/card*/device/pp_dpm_{kind}")):
+            try:
+                with open(path) as f:
+                    lines = [ln.strip() for ln in f if ln.strip()]
+            except OSError:
+                continue
+            if lines:
+                out[kind] = lines
+                break
+    return out or None
+
+
 def run_env(dev):
     """The device and software the numbers were taken on."""
     import torch
@@ -86,7 +118,8 @@ def run_env(dev):
         pass
     return {"device": props.name, "arch": getattr(props, "gcnArchName", None),
             "compute_units": props.multi_processor_count, "rocm": rocm,
-            "torch": torch.__version__, "hip": torch.version.hip}
+            "torch": torch.__version__, "hip": torch.version.hip,
+            "library_source_sha256": library_source_digest(), "clock_levels_mhz": clock_levels()}
 
 
 def cpu_model():

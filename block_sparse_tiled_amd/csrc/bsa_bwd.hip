@@ -254,6 +254,34 @@ __device__ __forceinline__ void dma_tile_part(const uint16_t* __restrict__ src, 
     dma16(srd, dl.off[it % DL::kN], soff, base + soff);
   }
 }
+// The copy dma_tile<T, D, kIsV, kSkip> makes, one instruction at a time:
+// set() takes the tile's source, LDS buffer and valid rows; one<it, kSkip>()
+// issues instruction `it` of this wave (with kSkip, not when its whole block
+// lies past the valid rows), so that a caller can spread a tile's copies over
+// other work.
+template <int T, int D, bool kIsV>
+struct TileCopy {
+  i32x4_t srd;
+  uint32_t base;
+  int rows;
+  __device__ __forceinline__ void set(const uint16_t* __restrict__ src, uint16_t* lds, int wave,
+                                      int valid_rows) {
+    base = launder_s(__builtin_amdgcn_readfirstlane(lds_address(lds)) + wave * 1024);
+    const uint64_t g = reinterpret_cast<uintptr_t>(src);
+    srd = i32x4_t{static_cast<int>(static_cast<uint32_t>(g)),
+                  static_cast<int>(static_cast<uint32_t>(g >> 32)), valid_rows * D * 2, 0x00020000};
+    rows = valid_rows;
+  }
+  template <int it, bool kSkip>
+  __device__ __forceinline__ void one(const DmaLane<T, D, kIsV>& dl, int wave) const {
+    using C = Cfg<T, D>;
+    constexpr int kRowsPerBlock = 512 / D;
+    constexpr uint32_t soff = it * C::kWaves * 1024;
+    if (!kSkip || (it * C::kWaves + wave) * kRowsPerBlock < rows)
+      dma16(srd, dl.off[it % DmaLane<T, D, kIsV>::kN], soff, base + soff);
+  }
+};
+
 template <int T, int D, int kLo, int kHi>
 __device__ __forceinline__ void zero_padding_part(uint16_t* lds, int vk, int wave, int lane) {
   using C = Cfg<T, D>;
