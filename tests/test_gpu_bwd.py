@@ -108,6 +108,21 @@ def test_duplicates_and_empty_tiles():
     check_problem(w, 2, "duplicates", max_k=3 * w.NT)
 
 
+@pytest.mark.parametrize("T,D", [(64, 64), (64, 128), (128, 64), (128, 128)])
+def test_long_transposed_lists(T, D):
+    """Every list names key tile 5, so that tile's transposed list is longer than one
+    compacted chunk of the dK/dV kernel (one entry per thread: 128 at T = 64, 256 at
+    T = 128) and its workgroup crosses chunk boundaries, with the next query tile's
+    copies in flight across each one; ragged lengths, NaN padding, a few duplicates."""
+    NT = 4 * T + 44  # two full chunks (2T entries each) and part of a third
+    vbs = [T] * NT
+    vbs[3], vbs[5], vbs[NT - 1] = T - 17, T - 1, 9
+    w = gen.random_problem(110 + T + D, B=1, H=1, D=D, T=T, vbs=vbs, counts=3, MS=3, pad="nan")
+    w.q2k_idx[..., 0] = 5  # may repeat one of the other two: a duplicate
+    print(f"bwd long transposed lists T={T} D={D} NT={NT}", flush=True)
+    check_problem(w, 12, f"long transposed lists T={T} D={D}", max_k=2 * NT)
+
+
 def test_tiny_config():
     w = gen.tiny()
     print("bwd tiny", flush=True)
