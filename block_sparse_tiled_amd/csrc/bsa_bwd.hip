@@ -130,6 +130,100 @@ __global__ __launch_bounds__(256) void k2q_kernel(const int32_t* __restrict__ q2
   if (lane == 0) k2q_num[wid] = count;  // the true count (the list holds the first max_k)
 }
 
+// The same lists by counting, for heads whose lists fit: one workgroup per
+// (head, range of J key tiles) counts in LDS, with 16-bit counters two to a
+// word, how often each list i names each key tile j of its range; then thread
+// jj walks i = 0 .. NT-1 and appends i as often as list i names j0 + jj.  The
+// counts fix the output, so the atomic increments leave it deterministic, and
+// it equals the scan's: ascending i, a tile named twice appearing twice.  The
+// pass over the lists is bound by load latency: each thread issues eight
+// loads, 1024 entries apart, before it uses any.
+constexpr int kCountWords = 16384;     // 64 KiB of counter pairs
+constexpr int kCountMaxTiles = 4096;   // the clamped list lengths staged in LDS
+constexpr int kCountThreads = 1024;
+__global__ __launch_bounds__(kCountThreads) void k2q_count_kernel(
+    const int32_t* __restrict__ q2k_idx, const int32_t* __restrict__ q2k_num, int num_tiles,
+    int max_sel, int span, int groups, int32_t* __restrict__ k2q_idx, int32_t* __restrict__ k2q_num,
+    int max_k) {
+  constexpr int kU = 8;
+  __shared__ uint32_t cnt[kCountWords];
+  __shared__ int nums[kCountMaxTiles];
+  const int64_t bh = blockIdx.x / groups;
+  const int j0 = static_cast<int>(blockIdx.x - bh * groups) * span;
+  const int tid = threadIdx.x;
+  const int NT = num_tiles, MS = max_sel, J = span;
+  const int words = NT * (J / 2);
+  for (int w = tid; w < words; w += kCountThreads) cnt[w] = 0;
+  const int32_t* num_h = q2k_num + bh * NT;
+  for (int i = tid; i < NT; i += kCountThreads) nums[i] = clampi(num_h[i], 0, MS);
+  __syncthreads();
+  if (MS > 0) {
+    // entry e = i * MS + pos; the thread's entries lie kCountThreads apart, so
+    // (i, pos) advances by (di, dp) with at most one carry
+    const int32_t* idx_h = q2k_idx + bh * static_cast<int64_t>(NT) * MS;
+    const uint32_t total = static_cast<uint32_t>(NT) * static_cast<uint32_t>(MS);
+    const uint32_t last = total - 1;
+    const int di = kCountThreads / MS, dp = kCountThreads % MS;
+    int i = tid / MS, pos = tid % MS;
+    for (uint32_t base = tid; base < total; base += kU * kCountThreads) {
+      int x[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const uint32_t e = base + u * kCountThreads;
+        x[u] = idx_h[e < total ? e : last];
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if (base + u * kCountThreads < total && pos < nums[i] && x[u] >= j0 && x[u] < j0 + J &&
+            x[u] < NT) {
+          const int jj = x[u] - j0;
+          atomicAdd(&cnt[(i * J + jj) >> 1], 1u << (16 * (jj & 1)));
+        }
+        pos += dp;
+        i += di;
+        if (pos >= MS) {
+          pos -= MS;
+          ++i;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // The walk, in parallel: key tile j0 + jj's rows are cut into R blocks,
+  // thread (r, jj) taking block r.  Pass 1 sums each block's counts (into the
+  // space of the list lengths, no longer needed); each thread's start is the
+  // sum over the blocks before it; pass 2 writes its entries from there.
+  const int R = kCountThreads / J;
+  const int jj = tid % J, r = tid / J, j = j0 + jj;
+  const bool walker = r < R && j < NT;
+  const int rows_per = (NT + R - 1) / R;
+  const int i_begin = r * rows_per < NT ? r * rows_per : NT;
+  const int i_end = i_begin + rows_per < NT ? i_begin + rows_per : NT;
+  const int shift = 16 * (jj & 1);
+  auto count_at = [&](int i) { return static_cast<int>((cnt[(i * J + jj) >> 1] >> shift) & 0xFFFFu); };
+  int sum = 0;
+  if (walker)
+#pragma unroll 4
+    for (int i = i_begin; i < i_end; ++i) sum += count_at(i);
+  __syncthreads();  // every thread is done with nums[]
+  int* part = nums;  // [R][J] block sums
+  if (r < R) part[r * J + jj] = walker ? sum : 0;
+  __syncthreads();
+  if (walker) {
+    int at = 0, total = 0;
+    for (int q = 0; q < R; ++q) {
+      const int v = part[q * J + jj];
+      at += q < r ? v : 0;
+      total += v;
+    }
+    if (r == 0) k2q_num[bh * NT + j] = total;
+    int32_t* dst = k2q_idx + (bh * NT + j) * static_cast<int64_t>(max_k);
+    for (int i = i_begin; i < i_end && at < max_k; ++i)
+      for (int c = count_at(i); c > 0; --c, ++at)
+        if (at < max_k) dst[at] = i;
+  }
+}
+
 // ---- D = rowsum(dO * (out + out_lo)) ------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void delta_kernel(const uint16_t* __restrict__ out,
@@ -836,6 +930,20 @@ hipError_t launch_grads(const bsa::BwdProblem& p, hipStream_t stream) {
 namespace bsa {
 
 hipError_t launch_k2q(const K2qProblem& p, hipStream_t stream) {
+  // Counting in LDS when the head's lengths fit and every workgroup's pass over the
+  // head's lists stays short; the scan otherwise.
+  if (p.num_tiles <= kCountMaxTiles && p.max_sel <= 65535) {
+    int span = 2 * (kCountWords / p.num_tiles);
+    if (span > kCountThreads) span = kCountThreads;
+    if (span > p.num_tiles + (p.num_tiles & 1)) span = p.num_tiles + (p.num_tiles & 1);
+    const int64_t groups = (p.num_tiles + span - 1) / span;
+    if (groups * p.num_tiles * static_cast<int64_t>(p.max_sel) <= (int64_t{1} << 22)) {
+      hipLaunchKernelGGL(k2q_count_kernel, dim3(static_cast<unsigned>(p.batch_heads * groups)),
+                         dim3(kCountThreads), 0, stream, p.q2k_idx, p.q2k_num, p.num_tiles, p.max_sel, span,
+                         static_cast<int>(groups), p.k2q_idx, p.k2q_num, p.max_k);
+      return hipGetLastError();
+    }
+  }
   const int64_t lists = p.batch_heads * p.num_tiles;
   const int64_t blocks = (lists + 3) / 4;
   hipLaunchKernelGGL(k2q_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,

@@ -123,6 +123,47 @@ def test_long_transposed_lists(T, D):
     check_problem(w, 12, f"long transposed lists T={T} D={D}", max_k=2 * NT)
 
 
+@pytest.mark.parametrize("B,H,NT,MS,max_k", [(2, 3, 300, 40, 50),     # counted in LDS
+                                             (1, 1, 4097, 2, 4097),    # more tiles than the count holds: scan
+                                             (1, 1, 1024, 1024, 64)])  # too many entries per head: scan
+def test_transposed_lists_both_forms(B, H, NT, MS, max_k):
+    """bsa_bwd_k2q, bit for bit against a plain transposition, in both of its forms
+    (counting in LDS, and the scan kept for heads too large to count): duplicates,
+    indices out of range (negative, NT, the int32 extremes), counts above MS and below
+    0 (clamped), and lists longer than max_k (cut, with the true length reported)."""
+    import torch
+
+    rng = np.random.default_rng(NT + MS)
+    idx = rng.integers(0, NT, size=(B, H, NT, MS)).astype(np.int32)  # duplicates likely
+    bad = rng.random(idx.shape) < 0.05
+    idx[bad] = rng.choice(np.array([-1, -5, NT, NT + 7, 2**31 - 1, -2**31], np.int64),
+                          size=int(bad.sum())).astype(np.int32)
+    num = rng.integers(-3, MS + 4, size=(B, H, NT)).astype(np.int32)
+    if NT >= 3:
+        idx[..., 0, :] = 2  # list 0 names tile 2 in every slot
+        num[..., 0] = MS
+    print(f"k2q B={B} H={H} NT={NT} MS={MS} max_k={max_k}", flush=True)
+    k2q_idx, k2q_num = bsa.bwd_k2q(to_dev(idx), to_dev(num), max_k=max_k)
+    torch.cuda.synchronize()
+    got_idx, got_num = k2q_idx.cpu().numpy(), k2q_num.cpu().numpy()
+    clamped = np.clip(num, 0, MS)
+    for b in range(B):
+        for h in range(H):
+            # plain transposition: for every list entry (ascending i, then position)
+            # naming an in-range tile j, append i to j's list
+            rows = np.repeat(np.arange(NT), MS).reshape(NT, MS)
+            live = (np.arange(MS)[None, :] < clamped[b, h][:, None]) & \
+                   (idx[b, h] >= 0) & (idx[b, h] < NT)
+            js, is_ = idx[b, h][live], rows[live]  # row-major: ascending i, then position
+            order = np.argsort(js, kind="stable")
+            counts = np.bincount(js, minlength=NT)
+            np.testing.assert_array_equal(got_num[b, h], counts, err_msg=f"b{b} h{h} counts")
+            starts = np.concatenate([[0], np.cumsum(counts)[:-1]])
+            for j in range(NT):
+                want = is_[order[starts[j]:starts[j] + counts[j]]][:max_k]
+                assert np.array_equal(got_idx[b, h, j, :len(want)], want), f"b{b} h{h} j{j}"
+
+
 def test_tiny_config():
     w = gen.tiny()
     print("bwd tiny", flush=True)
