@@ -12,9 +12,11 @@
 //
 // Kernels (all bf16 MFMA 32x32x16 with fp32 accumulation, operands staged in
 // LDS by LDS DMA with the forward's K-tile swizzle):
-//   - k2q_kernel: the transposed lists (for each key tile, the query tiles
-//     whose lists name it, ascending, a tile listed twice appearing twice),
-//     built deterministically: one wave per key tile scans the lists in
+//   - k2q_count_kernel / k2q_kernel: the transposed lists (for each key
+//     tile, the query tiles whose lists name it, ascending, a tile listed
+//     twice appearing twice), built deterministically: counted in LDS per
+//     (head, range of key tiles) and written by a parallel walk, or, for
+//     heads too large to count, one wave per key tile scanning the lists in
 //     order with a ballot-ordered append.
 //   - delta_kernel: D_r = dO_r . o_r in fp32 (0 for padding rows), with o_r
 //     the forward's fp32 result rebuilt as out + out_lo (the stored bf16
