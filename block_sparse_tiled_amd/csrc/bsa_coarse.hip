@@ -33,7 +33,8 @@
 //     order-preserving integer images (one ballot count per step), then the
 //     kept tiles written in ascending order through ballot prefix counts;
 //     also turns the row into softmax weights for the coarse output;
-//   - coarse_out_kernel: those weights times the pooled values, on fp32 MFMA;
+//   - coarse_out_kernel: those weights times the pooled values, on fp32 MFMA
+//     (the weight rows staged in LDS, one wave per 32 columns);
 //   - coarse_combine_kernel: out += gate * coarse output, valid rows only.
 #include <hip/hip_runtime.h>
 
@@ -103,17 +104,29 @@ __global__ __launch_bounds__(256) void coarse_logits_kernel(const float* __restr
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = 0.0f;
-  for (int d0 = 0; d0 < D; d0 += 32) {
-    // 64 rows x 32 columns of each operand: 8 values per thread
+  // 64 rows x 32 columns of each operand per round, 8 values per thread, the
+  // next round's loaded into registers while the current one is computed
+  float qv_next[8], kv_next[8];
+  auto load = [&](int d0) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int idx = tid + 256 * e;  // 0 .. 2047
       const int row = idx >> 5, dd = idx & 31;
       const int i = i0 + row, j = j0 + row;
-      qs[dd][row] = i < num_tiles ? qh[static_cast<int64_t>(i) * D + d0 + dd] : 0.0f;
-      ks[dd][row] = j < num_tiles ? kh[static_cast<int64_t>(j) * D + d0 + dd] : 0.0f;
+      qv_next[e] = i < num_tiles ? qh[static_cast<int64_t>(i) * D + d0 + dd] : 0.0f;
+      kv_next[e] = j < num_tiles ? kh[static_cast<int64_t>(j) * D + d0 + dd] : 0.0f;
+    }
+  };
+  load(0);
+  for (int d0 = 0; d0 < D; d0 += 32) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int idx = tid + 256 * e;
+      qs[idx & 31][idx >> 5] = qv_next[e];
+      ks[idx & 31][idx >> 5] = kv_next[e];
     }
     __syncthreads();
+    if (d0 + 32 < D) load(d0 + 32);
 #pragma unroll 4
     for (int dd = 0; dd < 32; ++dd) {
       const float4 qa = *reinterpret_cast<const float4*>(&qs[dd][4 * ty]);
@@ -251,48 +264,90 @@ __global__ __launch_bounds__(256) void coarse_select_kernel(
 // register r holds C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].  The order of the sum is
 // free here (the output is compared within a tolerance); the logits, which decide the
 // lists, are formed apart in a fixed order.
+// Coarse output rows i0 .. i0 + 31 of one head: wave c computes columns
+// 32c .. 32c + 31 over every key tile with v_mfma_f32_32x32x2f32 (A: 32 weight
+// rows x 2 key tiles, one value per lane; B: 2 pooled-value rows x 32
+// columns).  The weight rows and the pooled values of 128 key tiles at a time
+// are staged in LDS with coalesced loads, the next chunk's issued before the
+// current chunk's products (a lane's A value is one float of a different row,
+// so reading it from memory directly would leave each MFMA waiting on
+// scattered loads).
 template <int D>
 __global__ __launch_bounds__(256) void coarse_out_kernel(const float* __restrict__ w,
                                                          const float* __restrict__ vm,
                                                          int num_tiles, float* __restrict__ oc) {
-  __shared__ float part[3][16][64];
+  constexpr int kChunk = 128, kStride = kChunk + 1;  // padded weight rows: no bank conflicts
+  constexpr int kWLoads = 32 * kChunk / 256;         // weight floats per thread and chunk
+  constexpr int kVLoads = kChunk * D / 4 / 256;      // pooled-value float4s per thread and chunk
+  __shared__ float ws[32 * kStride];
+  __shared__ float4 vs[kChunk * D / 4];
   const int bh = blockIdx.z;
-  const int i0 = blockIdx.x * 32, c0 = blockIdx.y * 32;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i0 = blockIdx.x * 32;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 31, h = lane >> 5;
-  const int quarter = (num_tiles + 3) >> 2;
-  const int jq0 = wave * quarter;
-  const int jq1 = jq0 + quarter < num_tiles ? jq0 + quarter : num_tiles;
-  const int half_len = (quarter + 1) >> 1;
-  const int jb = jq0 + h * half_len;
-  const int i = i0 + r;
-  const float* wrow = w + (static_cast<int64_t>(bh) * num_tiles + (i < num_tiles ? i : 0)) * num_tiles;
-  const float* vh = vm + static_cast<int64_t>(bh) * num_tiles * D + c0 + r;
+  const int c0 = 32 * wave;
+  const float* wh = w + static_cast<int64_t>(bh) * num_tiles * num_tiles;
+  const float4* vh = reinterpret_cast<const float4*>(vm + static_cast<int64_t>(bh) * num_tiles * D);
+  const float* vsf = reinterpret_cast<const float*>(vs);
   f32x16_t acc = {};
-  constexpr int kU = 8;
-  for (int s0 = 0; s0 < half_len; s0 += kU) {
-    float a[kU], b[kU];
+  float wl[kWLoads];
+  float4 vl[kVLoads];
+  // chunk jc's loads into registers; they land while the previous chunk's
+  // products run
+  auto load = [&](int jc) {
+    const int n = num_tiles - jc < kChunk ? num_tiles - jc : kChunk;
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int step = s0 + u, j = jb + step;
-      const bool ok = step < half_len && j < jq1;
-      a[u] = ok && i < num_tiles ? wrow[j] : 0.0f;
-      b[u] = ok ? vh[static_cast<int64_t>(j) * D] : 0.0f;
+    for (int u = 0; u < kWLoads; ++u) {
+      const int e = tid + 256 * u, rr = e / kChunk, cc = e % kChunk, i = i0 + rr;
+      wl[u] = i < num_tiles && cc < n ? wh[static_cast<int64_t>(i) * num_tiles + jc + cc] : 0.0f;
     }
 #pragma unroll
-    for (int u = 0; u < kU; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[u], b[u], acc, 0, 0, 0);
-  }
-  if (wave > 0) {
+    for (int u = 0; u < kVLoads; ++u) {
+      const int e = tid + 256 * u, jj = e / (D / 4);
+      vl[u] = jj < n ? vh[static_cast<int64_t>(jc) * (D / 4) + e] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+  };
+  load(0);
+  for (int jc = 0; jc < num_tiles; jc += kChunk) {
+    __syncthreads();  // every wave is done with the previous chunk
 #pragma unroll
-    for (int g = 0; g < 16; ++g) part[wave - 1][g][lane] = acc[g];
+    for (int u = 0; u < kWLoads; ++u) {
+      const int e = tid + 256 * u;
+      ws[(e / kChunk) * kStride + e % kChunk] = wl[u];
+    }
+#pragma unroll
+    for (int u = 0; u < kVLoads; ++u) vs[tid + 256 * u] = vl[u];
+    __syncthreads();
+    if (jc + kChunk < num_tiles) load(jc + kChunk);
+    if (c0 < D) {
+      // operands read from LDS one batch of kB steps ahead of the MFMAs that use
+      // them; step t takes key tile 2t + h (zeros past the chunk's end)
+      constexpr int kB = 8, kSteps = kChunk / 2;
+      float a[2][kB], b[2][kB];
+      auto read = [&](int t0, int x) {
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+          const int j = 2 * (t0 + u) + h;
+          a[x][u] = ws[r * kStride + j];
+          b[x][u] = vsf[j * D + c0 + r];
+        }
+      };
+      read(0, 0);
+#pragma unroll
+      for (int t0 = 0; t0 < kSteps; t0 += kB) {
+        const int x = (t0 / kB) & 1;
+        if (t0 + kB < kSteps) read(t0 + kB, x ^ 1);
+#pragma unroll
+        for (int u = 0; u < kB; ++u)
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[x][u], b[x][u], acc, 0, 0, 0);
+      }
+    }
   }
-  __syncthreads();
-  if (wave != 0) return;
+  if (c0 >= D) return;
 #pragma unroll
   for (int g = 0; g < 16; ++g) {
-    const float v = acc[g] + part[0][g][lane] + part[1][g][lane] + part[2][g][lane];
     const int row = i0 + 8 * (g >> 2) + 4 * h + (g & 3);
-    if (row < num_tiles) oc[(static_cast<int64_t>(bh) * num_tiles + row) * D + c0 + r] = v;
+    if (row < num_tiles) oc[(static_cast<int64_t>(bh) * num_tiles + row) * D + c0 + r] = acc[g];
   }
 }
 
@@ -378,7 +433,7 @@ hipError_t launch_coarse_d(const bsa::CoarseProblem& p, hipStream_t stream) {
   err = hipGetLastError();
   if (err != hipSuccess || !weights) return err;
   hipLaunchKernelGGL(coarse_out_kernel<D>,
-                     dim3(static_cast<unsigned>((p.num_tiles + 31) / 32), D / 32,
+                     dim3(static_cast<unsigned>((p.num_tiles + 31) / 32), 1,
                           static_cast<unsigned>(p.batch_heads)),
                      dim3(256), 0, stream, logits, vm, p.num_tiles, p.coarse_out);
   return hipGetLastError();
