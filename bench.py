@@ -314,6 +314,38 @@ def run_coarse(args, w, put, dev):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+
+    # The layer's two orders, each from token-major Q, K, V and gate: the layout of the
+    # four tensors then bsa_coarse on the tile buffers, against the layout that also
+    # pools (bsa_tile_layout_pool) then bsa_coarse_pooled.
+    tok = [put(w.tok[x]) for x in ("q", "k", "v", "gate")]
+    src_map = put(w.tile_src_token)
+    tiled = [torch.empty((w.B, w.H, w.S, w.D), dtype=torch.bfloat16, device=dev) for _ in tok]
+    pooled = torch.empty((3, w.B, w.H, w.NT, w.D), dtype=torch.float32, device=dev)
+
+    def separate():
+        bsa.tile_layout(tok, src_map, w.T, outs=tiled)
+        bsa.coarse(tiled[0], tiled[1], tiled[2], vbs, w.T, topk, q2k_idx=idx, q2k_num=num,
+                   coarse_out=oc, workspace=ws)
+
+    def fused():
+        bsa.tile_layout_pool(tok, src_map, vbs, w.T, outs=tiled, pooled=pooled)
+        bsa.coarse_pooled(pooled, vbs, w.T, topk, q2k_idx=idx, q2k_num=num, coarse_out=oc,
+                          workspace=ws)
+
+    layer_ms = {}
+    for name, fn in (("layout_then_coarse_ms", separate), ("layout_pool_then_coarse_pooled_ms", fused)):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        evl = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for s in range(args.steps):
+            evl[s][0].record()
+            fn()
+            evl[s][1].record()
+        torch.cuda.synchronize()
+        layer_ms[name] = round(float(np.mean([e[0].elapsed_time(e[1]) for e in evl])), 5)
+
     valid = int(w.vbs.sum())
     pool_bytes = 3 * w.B * w.H * valid * w.D * 2 + 3 * w.B * w.H * w.NT * w.D * 4
     logit_flops = 2 * w.B * w.H * w.NT * w.NT * w.D
@@ -336,6 +368,7 @@ def run_coarse(args, w, put, dev):
                      "achieved": round(pool_bytes / (ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(pool_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                      "traffic": None},
+        "layer_orders": layer_ms,
     }
     print(json.dumps(rec), flush=True)
 

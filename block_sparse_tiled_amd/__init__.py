@@ -9,6 +9,7 @@ from .api import (  # noqa: F401
     bwd_k2q,
     coarse,
     coarse_combine,
+    coarse_pooled,
     coarse_workspace_size,
     cube_tile_map,
     fwd,
@@ -18,6 +19,7 @@ from .api import (  # noqa: F401
     load,
     status_string,
     tile_layout,
+    tile_layout_pool,
     tile_unlayout,
     within_launch_limits,
     within_launch_limits_py,

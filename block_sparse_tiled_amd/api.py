@@ -86,6 +86,12 @@ def load():
     lib.bsa_coarse.restype = ctypes.c_int
     lib.bsa_coarse_combine.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, i32, vp]
     lib.bsa_coarse_combine.restype = ctypes.c_int
+    lib.bsa_tile_layout_pool.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp, vp, i32,
+                                         i64, i64, i64, i64, i32, vp, vp]
+    lib.bsa_tile_layout_pool.restype = ctypes.c_int
+    lib.bsa_coarse_pooled.argtypes = [vp, vp, i32, i32, vp, vp, vp, i64, i64, i64, i32, i32, vp,
+                                      i64, vp]
+    lib.bsa_coarse_pooled.restype = ctypes.c_int
     lib.bsa_status_string.argtypes = [ctypes.c_int]
     lib.bsa_status_string.restype = ctypes.c_char_p
     lib.bsa_abi_version.argtypes = []
@@ -264,6 +270,57 @@ def tile_layout(srcs, tile_src_token, tile, outs=None):
         _check(lib.bsa_tile_layout(src_arr, dst_arr, len(srcs), _ptr(tile_src_token), tile,
                                    B, S_tok, H, NT, D, _stream_handle(device)))
     return outs
+
+
+def tile_layout_pool(srcs, tile_src_token, block_sizes, tile, outs=None, pooled=None):
+    """``tile_layout`` of Q, K, V (and optionally the gate: 3 or 4 tensors) that also forms
+    the coarse stage's pooled tiles from the rows it moves.  Returns (outs, pooled), pooled
+    float32 [3, B, H, NT, D] (the means of each tile's first block_sizes[t] rows of Q, K and
+    V), for ``coarse_pooled``."""
+    import torch
+
+    lib = load()
+    srcs = list(srcs)
+    if not 3 <= len(srcs) <= 4:
+        raise ValueError("tile_layout_pool takes Q, K, V and optionally the gate")
+    device = srcs[0].device
+    if device.type != "cuda":
+        raise ValueError("bsa.tile_layout_pool runs on a GPU")
+    for n, x in enumerate(srcs):
+        _require(x, f"src[{n}]", torch.bfloat16, device, 4)
+        if x.shape != srcs[0].shape:
+            raise ValueError("all layout inputs must share one shape")
+    _require(tile_src_token, "tile_src_token", torch.int32, device, 1)
+    B, S_tok, H, D = srcs[0].shape
+    rows = tile_src_token.shape[0]
+    if tile not in TILES or rows % tile:
+        raise ValueError("the map must cover a whole number of 64-, 128- or 256-row tiles")
+    NT = rows // tile
+    _require(block_sizes, "block_sizes", torch.int32, device, 1)
+    if tuple(block_sizes.shape) != (NT,):
+        raise ValueError("block_sizes must be [NT]")
+    if outs is None:
+        outs = [torch.empty((B, H, rows, D), dtype=torch.bfloat16, device=device) for _ in srcs]
+    else:
+        outs = list(outs)
+        if len(outs) != len(srcs):
+            raise ValueError("one output per input")
+        for n, o in enumerate(outs):
+            _require(o, f"out[{n}]", torch.bfloat16, device, 4)
+            if tuple(o.shape) != (B, H, rows, D):
+                raise ValueError("outputs must be [B, H, NT*tile, D]")
+    if pooled is None:
+        pooled = torch.empty((3, B, H, NT, D), dtype=torch.float32, device=device)
+    _require(pooled, "pooled", torch.float32, device, 5)
+    if tuple(pooled.shape) != (3, B, H, NT, D):
+        raise ValueError("pooled must be [3, B, H, NT, D]")
+    src_arr = (ctypes.c_void_p * len(srcs))(*[_ptr(x) for x in srcs])
+    dst_arr = (ctypes.c_void_p * len(outs))(*[_ptr(o) for o in outs])
+    with torch.cuda.device(device):
+        _check(lib.bsa_tile_layout_pool(src_arr, dst_arr, len(srcs), _ptr(tile_src_token),
+                                        _ptr(block_sizes), tile, B, S_tok, H, NT, D, _ptr(pooled),
+                                        _stream_handle(device)))
+    return outs, pooled
 
 
 def tile_unlayout(tiled, token_row, tile, tokens=None, outs=None):
@@ -456,6 +513,29 @@ def coarse_workspace_size(batch, heads, num_tiles, tile, head_dim):
     return int(n.value)
 
 
+def _coarse_outputs(device, B, H, NT, D, topk, max_sel, coarse_out, q2k_idx, q2k_num):
+    import torch
+
+    MS = int(topk if max_sel is None else max_sel)
+    if q2k_idx is None:
+        q2k_idx = torch.empty((B, H, NT, MS), dtype=torch.int32, device=device)
+    if q2k_num is None:
+        q2k_num = torch.empty((B, H, NT), dtype=torch.int32, device=device)
+    _require(q2k_idx, "q2k_idx", torch.int32, device, 4)
+    _require(q2k_num, "q2k_num", torch.int32, device, 3)
+    if tuple(q2k_idx.shape) != (B, H, NT, MS) or tuple(q2k_num.shape) != (B, H, NT):
+        raise ValueError("q2k_idx must be [B, H, NT, max_sel] and q2k_num [B, H, NT]")
+    oc = None
+    if coarse_out is True:
+        oc = torch.empty((B, H, NT, D), dtype=torch.float32, device=device)
+    elif coarse_out is not None and coarse_out is not False:
+        oc = coarse_out
+        _require(oc, "coarse_out", torch.float32, device, 4)
+        if tuple(oc.shape) != (B, H, NT, D):
+            raise ValueError("coarse_out must be [B, H, NT, D]")
+    return MS, q2k_idx, q2k_num, oc
+
+
 def coarse(q, k, v, block_sizes, tile, topk, max_sel=None, coarse_out=True, q2k_idx=None,
            q2k_num=None, workspace=None):
     """Coarse stage on tiled q, k, v [B, H, NT*tile, D] (bf16, cuda): each query tile's key
@@ -478,23 +558,8 @@ def coarse(q, k, v, block_sizes, tile, topk, max_sel=None, coarse_out=True, q2k_
     _require(block_sizes, "block_sizes", torch.int32, device, 1)
     if tuple(block_sizes.shape) != (NT,):
         raise ValueError("block_sizes must be [NT]")
-    MS = int(topk if max_sel is None else max_sel)
-    if q2k_idx is None:
-        q2k_idx = torch.empty((B, H, NT, MS), dtype=torch.int32, device=device)
-    if q2k_num is None:
-        q2k_num = torch.empty((B, H, NT), dtype=torch.int32, device=device)
-    _require(q2k_idx, "q2k_idx", torch.int32, device, 4)
-    _require(q2k_num, "q2k_num", torch.int32, device, 3)
-    if tuple(q2k_idx.shape) != (B, H, NT, MS) or tuple(q2k_num.shape) != (B, H, NT):
-        raise ValueError("q2k_idx must be [B, H, NT, max_sel] and q2k_num [B, H, NT]")
-    oc = None
-    if coarse_out is True:
-        oc = torch.empty((B, H, NT, D), dtype=torch.float32, device=device)
-    elif coarse_out is not None and coarse_out is not False:
-        oc = coarse_out
-        _require(oc, "coarse_out", torch.float32, device, 4)
-        if tuple(oc.shape) != (B, H, NT, D):
-            raise ValueError("coarse_out must be [B, H, NT, D]")
+    MS, q2k_idx, q2k_num, oc = _coarse_outputs(device, B, H, NT, D, topk, max_sel, coarse_out,
+                                               q2k_idx, q2k_num)
     with torch.cuda.device(device):
         need = coarse_workspace_size(B, H, NT, tile, D)
     if workspace is None:
@@ -504,6 +569,38 @@ def coarse(q, k, v, block_sizes, tile, topk, max_sel=None, coarse_out=True, q2k_
         _check(lib.bsa_coarse(_ptr(q), _ptr(k), _ptr(v), _ptr(block_sizes), tile, int(topk),
                               _ptr(q2k_idx), _ptr(q2k_num), _ptr(oc), B, H, NT, D, MS,
                               _ptr(workspace), workspace.numel(), _stream_handle(device)))
+    return q2k_idx, q2k_num, oc
+
+
+def coarse_pooled(pooled, block_sizes, tile, topk, max_sel=None, coarse_out=True, q2k_idx=None,
+                  q2k_num=None, workspace=None):
+    """``coarse`` from pooled tiles already formed by ``tile_layout_pool`` (float32
+    [3, B, H, NT, D]): the same lists, counts and coarse output, without reading q, k, v."""
+    import torch
+
+    lib = load()
+    device = pooled.device
+    if device.type != "cuda":
+        raise ValueError("the coarse stage runs on a GPU: pooled must be a cuda tensor")
+    _require(pooled, "pooled", torch.float32, device, 5)
+    _, B, H, NT, D = pooled.shape
+    if pooled.shape[0] != 3:
+        raise ValueError("pooled must be [3, B, H, NT, D]")
+    if tile not in TILES:
+        raise ValueError("tile must be 64, 128 or 256")
+    _require(block_sizes, "block_sizes", torch.int32, device, 1)
+    if tuple(block_sizes.shape) != (NT,):
+        raise ValueError("block_sizes must be [NT]")
+    MS, q2k_idx, q2k_num, oc = _coarse_outputs(device, B, H, NT, D, topk, max_sel, coarse_out,
+                                               q2k_idx, q2k_num)
+    need = 4 * B * H * NT * NT
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    _require(workspace, "workspace", torch.uint8, device, 1)
+    with torch.cuda.device(device):
+        _check(lib.bsa_coarse_pooled(_ptr(pooled), _ptr(block_sizes), tile, int(topk),
+                                     _ptr(q2k_idx), _ptr(q2k_num), _ptr(oc), B, H, NT, D, MS,
+                                     _ptr(workspace), workspace.numel(), _stream_handle(device)))
     return q2k_idx, q2k_num, oc
 
 

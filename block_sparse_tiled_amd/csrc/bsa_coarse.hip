@@ -394,15 +394,16 @@ unsigned stride_grid(int64_t threads) {
 template <int D>
 hipError_t launch_coarse_d(const bsa::CoarseProblem& p, hipStream_t stream) {
   const int64_t tiles_all = p.batch_heads * p.num_tiles;
-  float* qm = p.ws;
-  float* km = qm + tiles_all * D;
-  float* vm = km + tiles_all * D;
-  float* logits = vm + tiles_all * D;
-  {
+  // pooled rows: formed here (in the workspace, before the logits), or given
+  const float* qm = p.pooled ? p.pooled : p.ws;
+  const float* km = qm + tiles_all * D;
+  const float* vm = km + tiles_all * D;
+  float* logits = p.pooled ? p.ws : p.ws + 3 * tiles_all * D;
+  if (!p.pooled) {
     const int64_t threads = 3 * tiles_all * (D / 8);
     hipLaunchKernelGGL(coarse_pool_kernel<D>, dim3(stride_grid(threads)),
                        dim3(256), 0, stream, p.q, p.k, p.v, p.block_sizes, p.num_tiles, p.tile,
-                       tiles_all, qm);
+                       tiles_all, p.ws);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

@@ -55,9 +55,14 @@ struct LayoutProblem {
   int64_t heads;
   int64_t rows_per_head;  // num_tiles * tile
   int32_t head_dim;
+  // the layout with pooling only (launch_tile_layout_pool)
+  int32_t tile = 0;
+  const int32_t* block_sizes = nullptr;  // [num_tiles]
+  float* pooled = nullptr;               // [3, B*H*num_tiles, head_dim]
 };
 
 hipError_t launch_tile_layout(const LayoutProblem& p, hipStream_t stream);
+hipError_t launch_tile_layout_pool(const LayoutProblem& p, hipStream_t stream);
 
 // Transposed lists for the backward: for each key tile, the query tiles whose
 // lists name it (ascending; a tile listed twice appears twice).
@@ -111,7 +116,8 @@ struct CoarseProblem {
   int32_t* q2k_idx;   // [B, H, NT, max_sel]
   int32_t* q2k_num;   // [B, H, NT]
   float* coarse_out;  // [B, H, NT, D], or null
-  float* ws;          // coarse_workspace_bytes()
+  float* ws;          // coarse_workspace_bytes(), or the logits only when pooled is given
+  const float* pooled = nullptr;  // [3, B*H*NT, D] pooled Q, K, V already formed, or null
   int64_t batch_heads;
   int32_t num_tiles;
   int32_t tile;

@@ -21,6 +21,10 @@
 
 namespace {
 
+__device__ __forceinline__ int clampi_layout(int x, int lo, int hi) {
+  return x < lo ? lo : (x > hi ? hi : x);
+}
+
 struct Ptrs {
   const uint4* src[4];
   uint4* dst[4];
@@ -80,6 +84,67 @@ __global__ __launch_bounds__(256) void tile_layout_kernel(Ptrs p, int n_tensors,
 #pragma unroll
       for (int x = 0; x < 4; ++x)
         if (x < n_tensors) p.dst[x][out_off] = val[u][x];
+    }
+  }
+}
+
+// The layout with the coarse stage's pooling: one workgroup per (head, tile).
+// For each tensor, the whole workgroup moves the tile's rows (every load
+// issued before any store) and, for the first three (Q, K, V), keeps them in
+// LDS; then thread d sums column d over the rows below block_sizes[t] in
+// binary32, in row order, and divides by the count: the sums and quotients the
+// coarse stage forms from the tile buffer, so the pooled rows are the same
+// bits.  The tile's map entries are staged in LDS first.
+constexpr int kPoolMaxTile = 256;
+template <int D8>
+__global__ __launch_bounds__(256) void tile_layout_pool_kernel(
+    Ptrs p, int n_tensors, const int32_t* __restrict__ map, const int32_t* __restrict__ vbs,
+    int64_t tokens, int64_t heads, int num_tiles, int tile, int64_t tiles_all,
+    float* __restrict__ pooled) {
+  constexpr int D = 8 * D8;
+  __shared__ uint4 rows_s[kPoolMaxTile * D8];
+  __shared__ int32_t smap[kPoolMaxTile];
+  const int64_t bht = blockIdx.x;  // bh * num_tiles + t
+  const int64_t bh = bht / num_tiles;
+  const int t = static_cast<int>(bht - bh * num_tiles);
+  const int64_t b = bh / heads, h = bh - b * heads;
+  const int tid = threadIdx.x;
+  for (int s = tid; s < tile; s += 256) smap[s] = map[static_cast<int64_t>(t) * tile + s];
+  const int n = clampi_layout(vbs[t], 0, tile);
+  __syncthreads();
+  const int chunks = tile * D8;  // at most kPoolMaxTile * D8 = 16 per thread
+  const int64_t out0 = bht * chunks;
+  for (int x = 0; x < n_tensors; ++x) {
+    constexpr int kMax = kPoolMaxTile * D8 / 256;
+    uint4 val[kMax];
+#pragma unroll
+    for (int u = 0; u < kMax; ++u) {
+      const int e = tid + 256 * u;
+      val[u] = make_uint4(0u, 0u, 0u, 0u);
+      if (e < chunks) {
+        const int32_t tok = smap[e / D8];
+        if (tok >= 0 && tok < tokens) val[u] = p.src[x][((b * tokens + tok) * heads + h) * D8 + e % D8];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kMax; ++u) {
+      const int e = tid + 256 * u;
+      if (e < chunks) {
+        p.dst[x][out0 + e] = val[u];
+        if (x < 3) rows_s[e] = val[u];
+      }
+    }
+    if (x < 3) {
+      __syncthreads();
+      if (tid < D) {
+        const uint16_t* col = reinterpret_cast<const uint16_t*>(rows_s) + tid;
+        float acc = 0.0f;
+#pragma unroll 8
+        for (int s = 0; s < n; ++s)
+          acc = __fadd_rn(acc, __uint_as_float(static_cast<uint32_t>(col[s * D]) << 16));
+        pooled[(x * tiles_all + bht) * D + tid] = n > 0 ? __fdiv_rn(acc, static_cast<float>(n)) : 0.0f;
+      }
+      __syncthreads();  // every column is summed before the next tensor's rows land
     }
   }
 }
@@ -146,6 +211,26 @@ hipError_t launch_tile_layout(const LayoutProblem& lp, hipStream_t stream) {
                : (small ? reinterpret_cast<const void*>(&tile_layout_kernel<8, 4>)
                         : reinterpret_cast<const void*>(&tile_layout_kernel<8, 1>));
   return hipLaunchKernel(fn, grid, block, args, 0, stream);
+}
+
+hipError_t launch_tile_layout_pool(const LayoutProblem& lp, hipStream_t stream) {
+  Ptrs p;
+  for (int x = 0; x < 4; ++x) {
+    p.src[x] = static_cast<const uint4*>(lp.src[x]);
+    p.dst[x] = static_cast<uint4*>(lp.dst[x]);
+  }
+  const int d8 = lp.head_dim / 8;
+  int num_tiles = static_cast<int>(lp.rows_per_head / lp.tile);
+  int64_t tiles_all = lp.batch * lp.heads * num_tiles;
+  int n = lp.n_tensors, tile = lp.tile;
+  const int32_t* map = lp.tile_src_token;
+  const int32_t* vbs = lp.block_sizes;
+  int64_t tokens = lp.tokens, heads = lp.heads;
+  float* pooled = lp.pooled;
+  void* args[] = {&p, &n, &map, &vbs, &tokens, &heads, &num_tiles, &tile, &tiles_all, &pooled};
+  const void* fn = d8 == 16 ? reinterpret_cast<const void*>(&tile_layout_pool_kernel<16>)
+                            : reinterpret_cast<const void*>(&tile_layout_pool_kernel<8>);
+  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(tiles_all)), dim3(256), args, 0, stream);
 }
 
 hipError_t launch_tile_unlayout(const LayoutProblem& lp, hipStream_t stream) {

@@ -339,3 +339,40 @@ def test_noalloc_validates_like_fwd(lib):
     assert f(B=0) == OK
     assert f() in expected
     assert bsa.status_string(7) != "unknown status"
+
+
+def test_layout_pool_and_coarse_pooled_reject_bad_arguments(lib):
+    expected = {OK, NO_DEVICE, UNSUPPORTED}
+    arr = lambda *ps: (ctypes.c_void_p * len(ps))(*ps)  # noqa: E731
+    src, dst = arr(fake(0), fake(1), fake(2), fake(3)), arr(fake(4), fake(5), fake(6), fake(7))
+
+    def lp(n=3, tile=64, D=64, map_=fake(8), bs=fake(9), pooled=fake(10), B=1, H=1, NT=2, tok=100):
+        return lib.bsa_tile_layout_pool(src, dst, n, map_, bs, tile, B, tok, H, NT, D, pooled, NUL)
+
+    assert lp(n=2) == INVALID  # Q, K and V are needed
+    assert lp(n=5) == INVALID
+    assert lp(tile=96) == SHAPE
+    assert lp(D=32) == SHAPE
+    assert lp(bs=NUL) == INVALID
+    assert lp(pooled=NUL) == INVALID
+    assert lp(pooled=fake(0)) == INVALID  # pooled over an input
+    assert lp(pooled=fake(5)) == INVALID  # pooled over an output
+    assert lp(B=0, map_=NUL, bs=NUL, pooled=NUL) == OK
+    assert lp() in expected
+    assert lp(n=4) in expected
+
+    def cp(topk=2, max_sel=2, NT=4, tile=64, D=64, pooled=fake(0), ws=fake(7), ws_bytes=1 << 20,
+           outs=None):
+        o = [fake(4 + n) for n in range(3)] if outs is None else outs
+        return lib.bsa_coarse_pooled(pooled, fake(3), tile, topk, o[0], o[1], o[2], 1, 1, NT, D,
+                                     max_sel, ws, ws_bytes, NUL)
+
+    assert cp(topk=3) == INVALID
+    assert cp(tile=32) == SHAPE
+    assert cp(NT=4097) == SHAPE
+    assert cp(pooled=NUL) == INVALID
+    assert cp(ws=NUL) == INVALID
+    assert cp(ws_bytes=4 * 4 * 4 - 4) == INVALID  # the logits need 4 * NT^2 bytes per head
+    assert cp(ws_bytes=4 * 4 * 4) in expected
+    assert cp(outs=[fake(0), fake(5), fake(6)]) == INVALID  # lists over the pooled input
+    assert cp() in expected

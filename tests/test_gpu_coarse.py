@@ -187,3 +187,57 @@ def test_coarse_sweep(case):
     q, k, v, vbs, T, topk, max_sel, desc = draw_coarse_problem(case)
     print(f"coarse sweep {case}: {desc}", flush=True)
     check(q, k, v, vbs, T, topk, max_sel=max_sel, label=desc)
+
+
+def _layout_pool_case(name):
+    """A named configuration, or a small problem whose map has padding inside the valid
+    rows, tokens out of range and 256-row tiles, at D = 64."""
+    if name != "odd_map":
+        return gen.make(name, gate=True), name == "video"
+    rng = np.random.default_rng(77)
+    B, H, D, T, NT = 2, 3, 64, 256, 5
+    vbs = np.array([256, 0, 200, 1, 97], np.int32)
+    S_tok = 700
+    tok = {x: randn(rng, (B, S_tok, H, D)) for x in ("q", "k", "v", "gate")}
+    src = np.full(NT * T, -1, np.int32)
+    for t in range(NT):
+        src[t * T:t * T + vbs[t]] = rng.integers(0, S_tok, vbs[t])
+    src[2 * T + 5] = -1                  # padding inside tile 2's valid rows
+    src[4 * T + 3] = S_tok               # out of range: padding
+    src[4 * T + 4] = -(2**31)
+    w = gen.Workload(name="odd_map", B=B, H=H, D=D, T=T, NT=NT, q=None, k=None, v=None,
+                     q2k_idx=None, q2k_num=None, vbs=vbs, tok=tok, tile_src_token=src)
+    return w, False
+
+
+@pytest.mark.parametrize("name", ["video", "ragged", "odd_map"])
+def test_layout_pool_then_coarse_pooled(name):
+    """bsa_tile_layout_pool writes the tile buffers bsa_tile_layout writes and the pooled
+    tiles the oracle forms from them (bit for bit), and bsa_coarse_pooled on those gives
+    bsa_coarse's lists, counts and coarse output bit for bit."""
+    import torch
+
+    import oracle
+
+    w, with_gate = _layout_pool_case(name)
+    names = ("q", "k", "v", "gate") if with_gate else ("q", "k", "v")
+    tok = [to_dev(w.tok[x]) for x in names]
+    src_map, vbs = to_dev(w.tile_src_token), to_dev(w.vbs)
+    print(f"layout+pool {name}: B={w.B} H={w.H} NT={w.NT} T={w.T} D={w.D} tensors={len(tok)}",
+          flush=True)
+    tiled, pooled = bsa.tile_layout_pool(tok, src_map, vbs, w.T)
+    ref_tiled = bsa.tile_layout(tok, src_map, w.T)
+    torch.cuda.synchronize()
+    for x, (a, b) in enumerate(zip(tiled, ref_tiled)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"{name}: tensor {x}"
+    got = pooled.cpu().numpy()
+    for x in range(3):
+        want = oracle.coarse_pool(bits_from_dev(ref_tiled[x]), w.vbs, w.T)
+        np.testing.assert_array_equal(got[x].view(np.uint32), want.view(np.uint32),
+                                      err_msg=f"{name}: pooled tensor {x}")
+    topk = min(16, w.NT)
+    a = bsa.coarse(tiled[0], tiled[1], tiled[2], vbs, w.T, topk, max_sel=topk + 2)
+    b = bsa.coarse_pooled(pooled, vbs, w.T, topk, max_sel=topk + 2)
+    torch.cuda.synchronize()
+    for x, (ta, tb) in enumerate(zip(a, b)):
+        assert torch.equal(ta.view(torch.int32), tb.view(torch.int32)), f"{name}: coarse output {x}"
