@@ -341,3 +341,69 @@ def test_full_size_config(name, heads):
         dq_zero, dkv_zero = grad_zero_rows(s.q2k_idx, s.q2k_num, s.vbs, s.T)
         for key, r, z in zip(("dq", "dk", "dv"), ref, (dq_zero, dkv_zero, dkv_zero)):
             compare_grad(got[key][b:b + 1, h:h + 1], r, f"{name} b{b} h{h} {key}", z)
+
+
+def test_training_pass_graph_capture():
+    """The training pass (bsa_fwd_lse, bsa_bwd_k2q, bsa_bwd) on the ragged workload,
+    captured into a HIP graph on a fresh stream whose first library call happens inside
+    the capture; each replay, with eager work and a sync between, gives the eager
+    output, log-sum-exp, transposed lists and gradients bit for bit, and so does the
+    same pass on a second stream."""
+    import torch
+
+    w = gen.ragged()
+    q, k, v, idx, num, vbs = (to_dev(x) for x in (w.q, w.k, w.v, w.q2k_idx, w.q2k_num, w.vbs))
+    rng = np.random.default_rng(21)
+    dout = to_dev(gen.to_bf16_bits(rng.standard_normal(w.q.shape).astype(np.float32)))
+    shape = (w.B, w.H, w.S, w.D)
+    out, out_lo = (torch.empty(shape, dtype=torch.bfloat16, device="cuda") for _ in range(2))
+    lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device="cuda")
+    grads = [torch.empty(shape, dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    k2q = []
+
+    def step():
+        o, l, lo = bsa.fwd_lse(q, k, v, idx, num, vbs, w.T)
+        ki, kn = bsa.bwd_k2q(idx, num)
+        dq, dk, dv = bsa.bwd(q, k, v, o, lo, dout, l, idx, num, ki, kn, vbs, w.T)
+        for dst, src in zip([out, out_lo, lse] + grads, [o, lo, l, dq, dk, dv]):
+            dst.copy_(src)
+        k2q[:] = [ki, kn]
+
+    def snapshot(lists):
+        snap = [bits_from_dev(t) if t.dtype == torch.bfloat16 else t.cpu().numpy()
+                for t in [out, out_lo, lse] + grads + list(lists)]
+        ki, kn = snap[-2], snap[-1]  # only the first k2q_num entries of a list are written
+        snap[-2] = np.where(np.arange(ki.shape[3]) < np.minimum(kn, ki.shape[3])[..., None], ki, -1)
+        return snap
+
+    step()
+    torch.cuda.synchronize()
+    eager = snapshot(k2q)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        step()  # the first call on this stream
+    torch.cuda.synchronize()
+    graph_lists = list(k2q)  # the transposed lists live in the graph's memory
+    names = ["out", "out_lo", "lse", "dq", "dk", "dv", "k2q_idx", "k2q_num"]
+    for r in range(3):
+        for t in [out, out_lo] + grads + graph_lists:
+            t.fill_(-1 if t.dtype == torch.int32 else float("nan"))
+        lse.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(names, snapshot(graph_lists), eager):
+            np.testing.assert_array_equal(a, b, err_msg=f"replay {r}: {name}")
+        step()  # eager work between replays
+        torch.cuda.synchronize()
+        for name, a, b in zip(names, snapshot(k2q), eager):
+            np.testing.assert_array_equal(a, b, err_msg=f"eager after replay {r}: {name}")
+    other = torch.cuda.Stream()
+    with torch.cuda.stream(other):
+        step()
+    torch.cuda.synchronize()
+    for name, a, b in zip(names, snapshot(k2q), eager):
+        np.testing.assert_array_equal(a, b, err_msg=f"second stream: {name}")
