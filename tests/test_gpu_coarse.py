@@ -210,7 +210,7 @@ def _layout_pool_case(name):
     return w, False
 
 
-@pytest.mark.parametrize("name", ["video", "ragged", "odd_map"])
+@pytest.mark.parametrize("name", ["video", "ragged", "dense256", "odd_map"])
 def test_layout_pool_then_coarse_pooled(name):
     """bsa_tile_layout_pool writes the tile buffers bsa_tile_layout writes and the pooled
     tiles the oracle forms from them (bit for bit), and bsa_coarse_pooled on those gives
