@@ -376,3 +376,29 @@ def test_layout_pool_and_coarse_pooled_reject_bad_arguments(lib):
     assert cp(ws_bytes=4 * 4 * 4) in expected
     assert cp(outs=[fake(0), fake(5), fake(6)]) == INVALID  # lists over the pooled input
     assert cp() in expected
+
+
+def _declared_parameter_counts():
+    """{function: number of parameters} for every function include/bsa.h declares."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    counts = {}
+    for m in re.finditer(r"\b(bsa_[a-z_0-9]+)\s*\(([^;{]*?)\)\s*;", text):
+        params = m.group(2).strip()
+        counts[m.group(1)] = 0 if params in ("", "void") else params.count(",") + 1
+    return counts
+
+
+def test_binding_argument_counts_match_the_header(lib):
+    """Every entry point the binding declares argtypes for takes as many arguments as
+    include/bsa.h declares (a drift between the two would pass wrong values silently)."""
+    counts = _declared_parameter_counts()
+    assert sorted(counts) == _declared_functions()
+    checked = 0
+    for name, n in counts.items():
+        fn = getattr(lib, name)
+        if fn.argtypes is None:
+            continue
+        assert len(fn.argtypes) == n, f"{name}: header {n} parameters, binding {len(fn.argtypes)}"
+        checked += 1
+    assert checked == len(counts)  # the binding declares argtypes for every entry point
