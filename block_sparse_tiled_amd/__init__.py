@@ -4,6 +4,7 @@ The computation lives in ``libbsa.so`` (hand-written HIP kernels behind the C
 ABI in ``include/bsa.h``); this package only marshals arguments.
 """
 from .api import (  # noqa: F401
+    COARSE_MAX_TILES,
     BsaError,
     bwd,
     bwd_k2q,

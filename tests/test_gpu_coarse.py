@@ -74,6 +74,18 @@ def test_random_problems(T, D, NT, topk):
     check(q, k, v, vbs, T, topk, max_sel=topk + 3, label=f"T={T} D={D} NT={NT} topk={topk}")
 
 
+def test_most_tiles():
+    """BSA_COARSE_MAX_TILES tiles in one head (64-row tiles, D = 64): the widest
+    selection register block and eight chunks of the coarse output's staging."""
+    rng = np.random.default_rng(4096)
+    T, D, NT = 64, 64, bsa.COARSE_MAX_TILES
+    vbs = rng.integers(1, T + 1, NT).astype(np.int32)
+    vbs[rng.random(NT) < 0.05] = 0
+    q, k, v = (randn(rng, (1, 1, NT * T, D)) for _ in range(3))
+    print(f"coarse most tiles NT={NT}", flush=True)
+    check(q, k, v, vbs, T, 40, max_sel=41, label=f"NT={NT}")
+
+
 def test_ties_nan_and_every_tile():
     """Copies of one key tile give equal logits (the lower index is kept); a NaN in a
     valid key row ranks that tile as -inf; topk above the tile count keeps every
