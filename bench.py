@@ -315,26 +315,49 @@ def run_coarse(args, w, put, dev):
     wall = time.perf_counter() - t0
     ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
 
-    # The layer's two orders, each from token-major Q, K, V and gate: the layout of the
-    # four tensors then bsa_coarse on the tile buffers, against the layout that also
-    # pools (bsa_tile_layout_pool) then bsa_coarse_pooled.
+    # The whole layer, from token-major Q, K, V and gate to the token-major output, in
+    # its two orders: layout of the four tensors, coarse stage, fine attention on the
+    # coarse stage's lists, combine, way back; against the layout that also pools,
+    # the coarse stage from the pooled tiles, the fine attention, and the combine done
+    # in the way back.  (And the first two steps of each, on their own.)
     tok = [put(w.tok[x]) for x in ("q", "k", "v", "gate")]
     src_map = put(w.tile_src_token)
+    src_np = np.asarray(w.tile_src_token)
+    token_row_np = np.full(w.tok["q"].shape[1], -1, np.int32)
+    token_row_np[src_np[src_np >= 0]] = np.nonzero(src_np >= 0)[0]
+    token_row = put(token_row_np)
     tiled = [torch.empty((w.B, w.H, w.S, w.D), dtype=torch.bfloat16, device=dev) for _ in tok]
     pooled = torch.empty((3, w.B, w.H, w.NT, w.D), dtype=torch.float32, device=dev)
+    fine = torch.empty((w.B, w.H, w.S, w.D), dtype=torch.bfloat16, device=dev)
+    layer_out = torch.empty(tuple(w.tok["q"].shape), dtype=torch.bfloat16, device=dev)
+    fws = bsa.workspace_size(w.B, w.H, w.NT, w.T, w.D, topk)
+    fwd_ws = torch.empty(fws, dtype=torch.uint8, device=dev) if fws else None
 
-    def separate():
+    def separate_head():
         bsa.tile_layout(tok, src_map, w.T, outs=tiled)
         bsa.coarse(tiled[0], tiled[1], tiled[2], vbs, w.T, topk, q2k_idx=idx, q2k_num=num,
                    coarse_out=oc, workspace=ws)
 
-    def fused():
+    def fused_head():
         bsa.tile_layout_pool(tok, src_map, vbs, w.T, outs=tiled, pooled=pooled)
         bsa.coarse_pooled(pooled, vbs, w.T, topk, q2k_idx=idx, q2k_num=num, coarse_out=oc,
                           workspace=ws)
 
+    def separate_layer():
+        separate_head()
+        bsa.fwd(tiled[0], tiled[1], tiled[2], idx, num, vbs, w.T, out=fine, workspace=fwd_ws)
+        bsa.coarse_combine(fine, tiled[3], oc, vbs, w.T)
+        bsa.tile_unlayout([fine], token_row, w.T, outs=[layer_out])
+
+    def fused_layer():
+        fused_head()
+        bsa.fwd(tiled[0], tiled[1], tiled[2], idx, num, vbs, w.T, out=fine, workspace=fwd_ws)
+        bsa.tile_unlayout_combine(fine, tiled[3], oc, vbs, token_row, w.T, dst=layer_out)
+
     layer_ms = {}
-    for name, fn in (("layout_then_coarse_ms", separate), ("layout_pool_then_coarse_pooled_ms", fused)):
+    for name, fn in (("layout_then_coarse_ms", separate_head),
+                     ("layout_pool_then_coarse_pooled_ms", fused_head),
+                     ("layer_ms", separate_layer), ("layer_fused_ms", fused_layer)):
         for _ in range(args.warmup):
             fn()
         torch.cuda.synchronize()

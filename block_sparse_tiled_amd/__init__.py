@@ -22,6 +22,7 @@ from .api import (  # noqa: F401
     tile_layout,
     tile_layout_pool,
     tile_unlayout,
+    tile_unlayout_combine,
     within_launch_limits,
     within_launch_limits_py,
     workspace_size,

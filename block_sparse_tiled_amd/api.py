@@ -92,6 +92,9 @@ def load():
     lib.bsa_coarse_pooled.argtypes = [vp, vp, i32, i32, vp, vp, vp, i64, i64, i64, i32, i32, vp,
                                       i64, vp]
     lib.bsa_coarse_pooled.restype = ctypes.c_int
+    lib.bsa_tile_unlayout_combine.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, i64, i32, vp,
+                                              vp]
+    lib.bsa_tile_unlayout_combine.restype = ctypes.c_int
     lib.bsa_status_string.argtypes = [ctypes.c_int]
     lib.bsa_status_string.restype = ctypes.c_char_p
     lib.bsa_abi_version.argtypes = []
@@ -625,3 +628,37 @@ def coarse_combine(out, gate, coarse_out, block_sizes, tile):
         _check(lib.bsa_coarse_combine(_ptr(out), _ptr(gate), _ptr(coarse_out), _ptr(block_sizes),
                                       tile, B, H, NT, D, _stream_handle(device)))
     return out
+
+
+def tile_unlayout_combine(out, gate, coarse_out, block_sizes, token_row, tile, tokens=None,
+                          dst=None):
+    """``coarse_combine`` then ``tile_unlayout`` in one pass, leaving ``out`` unchanged:
+    the layer output gathered to token-major bf16 [B, S_tok, H, D]."""
+    import torch
+
+    lib = load()
+    device = out.device
+    _require(out, "out", torch.bfloat16, device, 4)
+    _require(gate, "gate", torch.bfloat16, device, 4)
+    _require(coarse_out, "coarse_out", torch.float32, device, 4)
+    _require(block_sizes, "block_sizes", torch.int32, device, 1)
+    _require(token_row, "token_row", torch.int32, device, 1)
+    B, H, S, D = out.shape
+    if gate.shape != out.shape or tile not in TILES or S % tile:
+        raise ValueError("gate must have out's shape and tile divide the sequence")
+    NT = S // tile
+    if tuple(coarse_out.shape) != (B, H, NT, D) or tuple(block_sizes.shape) != (NT,):
+        raise ValueError("coarse_out must be [B, H, NT, D] and block_sizes [NT]")
+    S_tok = int(token_row.shape[0]) if tokens is None else int(tokens)
+    if token_row.shape[0] != S_tok:
+        raise ValueError("token_row must have one entry per token")
+    if dst is None:
+        dst = torch.empty((B, S_tok, H, D), dtype=torch.bfloat16, device=device)
+    _require(dst, "dst", torch.bfloat16, device, 4)
+    if tuple(dst.shape) != (B, S_tok, H, D):
+        raise ValueError("dst must be [B, S_tok, H, D]")
+    with torch.cuda.device(device):
+        _check(lib.bsa_tile_unlayout_combine(_ptr(out), _ptr(gate), _ptr(coarse_out),
+                                             _ptr(block_sizes), _ptr(token_row), tile, B, S_tok, H,
+                                             NT, D, _ptr(dst), _stream_handle(device)))
+    return dst

@@ -351,6 +351,22 @@ __global__ __launch_bounds__(256) void coarse_out_kernel(const float* __restrict
   }
 }
 
+// 8 bf16 outputs of one row, out + gate * coarse output in fp32, then one
+// rounding (RNE) to bf16: the combine's arithmetic, shared by both kernels
+// that apply it so that they give the same bits.
+__device__ __forceinline__ uint4 combine_chunk(uint4 o, uint4 gt, const float* __restrict__ cv) {
+  const uint32_t ow[4] = {o.x, o.y, o.z, o.w}, gw[4] = {gt.x, gt.y, gt.z, gt.w};
+  uint32_t res[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float lo = __uint_as_float(ow[e] << 16) + __uint_as_float(gw[e] << 16) * cv[2 * e];
+    const float hi = __uint_as_float(ow[e] & 0xffff0000u) +
+                     __uint_as_float(gw[e] & 0xffff0000u) * cv[2 * e + 1];
+    res[e] = __builtin_bit_cast(uint32_t, to_bf16x2(lo, hi));
+  }
+  return make_uint4(res[0], res[1], res[2], res[3]);
+}
+
 // ---- out += gate * coarse output of the row's tile (valid rows only) ----------------------
 template <int D>
 __global__ __launch_bounds__(256) void coarse_combine_kernel(uint16_t* __restrict__ out,
@@ -372,16 +388,44 @@ __global__ __launch_bounds__(256) void coarse_combine_kernel(uint16_t* __restric
   const uint4 o = *po;
   const uint4 gt = *reinterpret_cast<const uint4*>(gate + row * D + 8 * c);
   const float* cv = oc + bht * D + 8 * c;
-  const uint32_t ow[4] = {o.x, o.y, o.z, o.w}, gw[4] = {gt.x, gt.y, gt.z, gt.w};
-  uint32_t res[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float lo = __uint_as_float(ow[e] << 16) + __uint_as_float(gw[e] << 16) * cv[2 * e];
-    const float hi = __uint_as_float(ow[e] & 0xffff0000u) +
-                     __uint_as_float(gw[e] & 0xffff0000u) * cv[2 * e + 1];
-    res[e] = __builtin_bit_cast(uint32_t, to_bf16x2(lo, hi));
+  *po = combine_chunk(o, gt, cv);
   }
-  *po = make_uint4(res[0], res[1], res[2], res[3]);
+}
+
+// The combine and the way back in one pass: token-major output row n of head h
+// is tile row r = token_row[n] of the fine output, combined as above when r is
+// a valid row of its tile and passed through otherwise (the padding rows the
+// combine leaves alone), or +0 when r is out of range: the bits bsa_tile_unlayout
+// gives after bsa_coarse_combine, without writing the tile buffer back.  One
+// 16-byte chunk per thread, chunk index fastest, then head, then token.
+template <int D>
+__global__ __launch_bounds__(256) void unlayout_combine_kernel(
+    const uint16_t* __restrict__ out, const uint16_t* __restrict__ gate,
+    const float* __restrict__ oc, const int32_t* __restrict__ vbs,
+    const int32_t* __restrict__ token_row, int64_t tokens, int64_t heads, int num_tiles, int tile,
+    uint16_t* __restrict__ dst) {
+  constexpr int kChunks = D / 8;
+  const int64_t b = blockIdx.y;
+  const int64_t chunks = tokens * heads * kChunks;  // per batch
+  const int64_t rows_per_head = static_cast<int64_t>(num_tiles) * tile;
+  for (int64_t g = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; g < chunks;
+       g += static_cast<int64_t>(gridDim.x) * 256) {
+    const int c = static_cast<int>(g % kChunks);
+    const int64_t th = g / kChunks;  // token * heads + head
+    const int64_t n = th / heads;
+    const int64_t h = th - n * heads;
+    const int32_t r = token_row[n];
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (r >= 0 && r < rows_per_head) {
+      const int64_t bh = b * heads + h;
+      const int64_t off = (bh * rows_per_head + r) * D + 8 * c;
+      v = *reinterpret_cast<const uint4*>(out + off);
+      const int t = r / tile;
+      if (r - t * tile < clampi(vbs[t], 0, tile))
+        v = combine_chunk(v, *reinterpret_cast<const uint4*>(gate + off),
+                          oc + (bh * num_tiles + t) * D + 8 * c);
+    }
+    *reinterpret_cast<uint4*>(dst + (b * chunks + g) * 8) = v;
   }
 }
 
@@ -451,6 +495,21 @@ size_t coarse_workspace_bytes(int64_t batch_heads, int64_t num_tiles, int32_t he
 
 hipError_t launch_coarse(const CoarseProblem& p, hipStream_t stream) {
   return p.head_dim == 128 ? launch_coarse_d<128>(p, stream) : launch_coarse_d<64>(p, stream);
+}
+
+hipError_t launch_unlayout_combine(const UnlayoutCombineProblem& p, hipStream_t stream) {
+  const int64_t chunks = p.tokens * p.heads * (p.head_dim / 8);
+  const int64_t want = (chunks + 255) / 256;
+  const dim3 grid(static_cast<unsigned>(want < 65536 ? want : 65536), static_cast<unsigned>(p.batch));
+  if (p.head_dim == 128)
+    hipLaunchKernelGGL(unlayout_combine_kernel<128>, grid, dim3(256), 0, stream, p.out, p.gate,
+                       p.coarse_out, p.block_sizes, p.token_row, p.tokens, p.heads, p.num_tiles,
+                       p.tile, p.dst);
+  else
+    hipLaunchKernelGGL(unlayout_combine_kernel<64>, grid, dim3(256), 0, stream, p.out, p.gate,
+                       p.coarse_out, p.block_sizes, p.token_row, p.tokens, p.heads, p.num_tiles,
+                       p.tile, p.dst);
+  return hipGetLastError();
 }
 
 hipError_t launch_coarse_combine(const CombineProblem& p, hipStream_t stream) {

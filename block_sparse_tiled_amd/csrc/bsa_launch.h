@@ -129,6 +129,24 @@ struct CoarseProblem {
 size_t coarse_workspace_bytes(int64_t batch_heads, int64_t num_tiles, int32_t head_dim);
 hipError_t launch_coarse(const CoarseProblem& p, hipStream_t stream);
 
+// The combine and the inverse gather in one pass (bsa_tile_unlayout_combine).
+struct UnlayoutCombineProblem {
+  const uint16_t* out;          // [B, H, NT*T, D] fine output (read only)
+  const uint16_t* gate;         // [B, H, NT*T, D]
+  const float* coarse_out;      // [B, H, NT, D]
+  const int32_t* block_sizes;   // [NT]
+  const int32_t* token_row;     // [tokens]
+  uint16_t* dst;                // [B, tokens, H, D]
+  int64_t batch;
+  int64_t tokens;
+  int64_t heads;
+  int32_t num_tiles;
+  int32_t tile;
+  int32_t head_dim;
+};
+
+hipError_t launch_unlayout_combine(const UnlayoutCombineProblem& p, hipStream_t stream);
+
 struct CombineProblem {
   uint16_t* out;           // [B, H, NT*T, D], updated in place
   const uint16_t* gate;    // [B, H, NT*T, D]

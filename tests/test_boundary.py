@@ -402,3 +402,24 @@ def test_binding_argument_counts_match_the_header(lib):
         assert len(fn.argtypes) == n, f"{name}: header {n} parameters, binding {len(fn.argtypes)}"
         checked += 1
     assert checked == len(counts)  # the binding declares argtypes for every entry point
+
+
+def test_unlayout_combine_rejects_bad_arguments(lib):
+    expected = {OK, NO_DEVICE, UNSUPPORTED}
+
+    def uc(out=fake(0), gate=fake(1), oc=fake(2), bs=fake(3), rows=fake(4), dst=fake(5), tile=64,
+           D=64, B=1, H=1, tok=100, NT=2):
+        return lib.bsa_tile_unlayout_combine(out, gate, oc, bs, rows, tile, B, tok, H, NT, D, dst,
+                                             NUL)
+
+    assert uc(tile=96) == SHAPE
+    assert uc(D=32) == SHAPE
+    assert uc(B=-1) == INVALID
+    assert uc(dst=NUL) == INVALID
+    assert uc(rows=NUL) == INVALID
+    assert uc(gate=NUL) == INVALID
+    assert uc(dst=fake(0)) == INVALID  # dst over the fine output
+    assert uc(dst=ctypes.c_void_p(fake(4).value + 8)) == INVALID  # dst over the token map
+    assert uc(tok=0, rows=NUL, dst=NUL) == OK
+    assert uc(NT=0, out=NUL, gate=NUL, oc=NUL, bs=NUL) in expected  # every token +0
+    assert uc() in expected

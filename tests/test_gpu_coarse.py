@@ -253,3 +253,37 @@ def test_layout_pool_then_coarse_pooled(name):
     torch.cuda.synchronize()
     for x, (ta, tb) in enumerate(zip(a, b)):
         assert torch.equal(ta.view(torch.int32), tb.view(torch.int32)), f"{name}: coarse output {x}"
+
+
+@pytest.mark.parametrize("name", ["video", "ragged"])
+def test_unlayout_combine_matches_the_two_calls(name):
+    """bsa_tile_unlayout_combine gives the bits of bsa_coarse_combine then
+    bsa_tile_unlayout (tokens mapped to padding rows and out-of-range rows included)
+    and leaves the fine output unchanged."""
+    import torch
+
+    w = gen.make(name, gate=True)
+    q, k, v = (to_dev(x) for x in (w.q, w.k, w.v))
+    vbs = to_dev(w.vbs)
+    (gate,) = bsa.tile_layout([to_dev(w.tok["gate"])], to_dev(w.tile_src_token), w.T)
+    idx, num, oc = bsa.coarse(q, k, v, vbs, w.T, min(16, w.NT))
+    out = bsa.fwd(q, k, v, idx, num, vbs, w.T)
+    S_tok = w.tok["q"].shape[1]
+    src = w.tile_src_token
+    rows = np.full(S_tok, -1, np.int32)
+    ok = src >= 0
+    rows[src[ok]] = np.nonzero(ok)[0]
+    rows[::97] = w.NT * w.T + 5   # out of range: +0
+    pad = np.nonzero(~ok)[0]
+    if pad.size:
+        rows[1::89] = pad[0]      # a padding row of its tile: passed through unchanged
+    token_row = to_dev(rows)
+    print(f"unlayout+combine {name}: tokens={S_tok}", flush=True)
+    before = out.clone()
+    got = bsa.tile_unlayout_combine(out, gate, oc, vbs, token_row, w.T)
+    combined = out.clone()
+    bsa.coarse_combine(combined, gate, oc, vbs, w.T)
+    (want,) = bsa.tile_unlayout([combined], token_row, w.T)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), before.view(torch.int16)), "out was modified"
+    assert torch.equal(got.view(torch.int16), want.view(torch.int16)), f"{name}: layer output"
