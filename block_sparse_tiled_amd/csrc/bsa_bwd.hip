@@ -34,8 +34,12 @@
 //     per query tile of its transposed list, in blocks of 32 queries: S =
 //     Q K^T, P, dP = dO V^T, dS, then dV^T += dO^T P and dK^T += Q^T dS (dO^T
 //     and Q^T through the LDS transpose read).  K and V stay in registers.
-//     The next block's S and dP products are interleaved with the current
-//     block's dV/dK products, so that the softmax work runs beside MFMAs.
+//     The blocks are software-pipelined (kDkvPipe): at D = 128, with two
+//     register sets for S/dP and P/dS, one block's dV/dK products, a later
+//     block's S/dP products and the next block's softmax share each period;
+//     at D = 64 the next block's S/dP products go between the current block's
+//     dV/dK products.  At D = 128 the next query tile's copies are issued one
+//     instruction at a time among the products.
 //   The C-layout-to-B-operand reuse and the key (query) order within a
 //   16-wide chunk are those of the forward (bsa_fwd_common.h).
 //
