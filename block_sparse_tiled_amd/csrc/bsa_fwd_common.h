@@ -264,41 +264,6 @@ __device__ __forceinline__ int compact_list(const int32_t* __restrict__ list, in
   return __builtin_amdgcn_readfirstlane(total);
 }
 
-// Uniform read of one int32 through the scalar cache.  The tile lists and
-// lengths are read-only for the whole launch; as asm the read is issued as a
-// scalar load even though the (volatile) DMA statements keep the compiler
-// from proving that, and it never touches the vector-memory counter the
-// DMA waits rely on.
-__device__ __forceinline__ int scalar_load(const int32_t* p) {
-  // the address is uniform, but the compiler may have computed it in vector
-  // registers; s_load needs it in a scalar register pair
-  // (readfirstlane returns int: widen through uint32_t, never sign-extend)
-  const uint64_t a = reinterpret_cast<uint64_t>(p);
-  const uint64_t lo =
-      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a)));
-  const uint64_t hi =
-      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32)));
-  p = reinterpret_cast<const int32_t*>((hi << 32) | lo);
-  int v;
-  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p));
-  // asm results count as divergent; say it is uniform so indices derived
-  // from it stay in scalar registers
-  return __builtin_amdgcn_readfirstlane(v);
-}
-
-// Next usable list entry at or after n: in range and with at least one key.
-__device__ __forceinline__ int next_tile(const int32_t* __restrict__ list, int count,
-                                         const int32_t* __restrict__ vbs, int num_tiles, int T,
-                                         int& n, int& vk) {
-  for (; n < count; ++n) {
-    const int j = scalar_load(list + n);
-    if (j < 0 || j >= num_tiles) continue;
-    vk = clampi(scalar_load(vbs + j), 0, T);
-    if (vk > 0) return j;
-  }
-  return -1;
-}
-
 // max(m, a, b), ignoring quiet NaNs.  Written as asm because the compiler
 // wraps fmaxf on values it cannot prove canonical (such as MFMA results) in
 // extra canonicalising moves.  The compiler does not insert the wait states an
