@@ -514,18 +514,28 @@ void dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             dp[b2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 read_rows<D>(vs, 32 * (2 * hh + b2), kk, col, half), dop[kk], kk ? dp[b2] : zero16, 0, 0, 0);
           }
-        // P^T = exp2(S^T c - lse2) with keys at or past vk masked; dS^T = P^T (dP^T - D)
+        // P^T = exp2(S^T c - lse2) with keys at or past vk masked; dS^T = P^T (dP^T - D).
+        // A masked logit is selected to -inf, so its p is exp2(-inf) = 0 (a row whose
+        // lse is -inf or NaN is NaN through its valid keys in any case, or is padding),
+        // and its dS is 0 * (0 - D) (V padding rows are zero in LDS): a zero, of
+        // either sign, which leaves every dQ sum as the plain formula has it.
 #pragma unroll
         for (int b2 = 0; b2 < 2; ++b2) {
           const int kb = 2 * hh + b2;
-          const int t0 = vk - 32 * kb - 4 * half;
+          if (32 * kb + 32 > vk) {  // only the blocks that reach vk take the mask (uniform)
+            const int t0 = vk - 32 * kb - 4 * half;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const bool masked = 8 * (r >> 2) + (r & 3) >= t0;
-            const float p = masked ? 0.0f : __builtin_amdgcn_exp2f(__builtin_fmaf(s[b2][r], c, -lse2));
-            s[b2][r] = masked ? 0.0f : p * (dp[b2][r] - dlt);
+            for (int r = 0; r < 16; ++r)
+              if (8 * (r >> 2) + (r & 3) >= t0) s[b2][r] = -INFINITY;
           }
         }
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b2][r], c, -lse2));
+            s[b2][r] = p * (dp[b2][r] - dlt);
+          }
         // dQ^T += K^T dS^T over the four 16-key chunks of this half
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
