@@ -504,6 +504,11 @@ void dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         if constexpr (hh > 0)
           if (j2 >= 0) copy_half(std::integral_constant<int, hh - 1>{}, j2, vk2);
         if (wave * 32 < vq) {  // a wave whose rows are all padding computes nothing
+        // Raised issue priority for the S/dP products: two workgroups share each
+        // SIMD, and the wave in this phase winning issue pushes the pair towards
+        // anti-phase, one wave's exponentials and dQ products under the other's
+        // S/dP products.
+        __builtin_amdgcn_s_setprio(1);
         f32x16_t s[2], dp[2];
 #pragma unroll
         for (int kk = 0; kk < C::kKSteps; ++kk)
@@ -514,6 +519,7 @@ void dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             dp[b2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 read_rows<D>(vs, 32 * (2 * hh + b2), kk, col, half), dop[kk], kk ? dp[b2] : zero16, 0, 0, 0);
           }
+        __builtin_amdgcn_s_setprio(0);
         // P^T = exp2(S^T c - lse2) with keys at or past vk masked; dS^T = P^T (dP^T - D).
         // A masked logit is selected to -inf, so its p is exp2(-inf) = 0 (a row whose
         // lse is -inf or NaN is NaN through its valid keys in any case, or is padding),
