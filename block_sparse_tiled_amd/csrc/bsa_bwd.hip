@@ -477,6 +477,12 @@ void dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       dma_tile_part<T, D, h * kHP, (h + 1) * kHP>(kh + static_cast<int64_t>(j) * T * D, ks, wave, dl, vk);
       dma_tile_part<T, D, h * kHP, (h + 1) * kHP>(vh + static_cast<int64_t>(j) * T * D, vs, wave, dl, vk);
     };
+    // Q, dO and the row statistics must be in registers before the first copy:
+    // the copies are invisible to the compiler's wait-count bookkeeping, and a
+    // drain here, on every path into the tile loop, keeps it from placing
+    // waits for those loads inside the loop, where they would also wait for
+    // the copies in flight.
+    wait_vmcnt<0>();
     for (int t = 0; t < total; ++t) {
       const int2 e = tl[t];
       const int j = __builtin_amdgcn_readfirstlane(e.x);
@@ -487,10 +493,7 @@ void dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         j2 = __builtin_amdgcn_readfirstlane(e2.x);
         vk2 = __builtin_amdgcn_readfirstlane(e2.y);
       }
-      if (t == 0) {
-        wait_vmcnt<0>();  // the operands loaded above
-        static_for<NH>([&](auto hc) { copy_half(hc, j, vk); });
-      }
+      if (t == 0) static_for<NH>([&](auto hc) { copy_half(hc, j, vk); });
       static_for<NH>([&](auto hc) {  // 64 keys: key blocks 2*hh, 2*hh + 1
         constexpr int hh = decltype(hc)::value;
         // half hh of this tile has landed; issued after it: its later halves
