@@ -158,7 +158,8 @@ def fwd_out_shape(q_shape):
 
 def workspace_size(batch, heads, num_tiles, tile, head_dim, max_sel):
     """Bytes of workspace ``fwd`` and ``fwd_lse`` use for this shape on the current
-    device (0 when the call never cuts tile lists)."""
+    device: per-XCD work-queue counters for long launches and the partials of split
+    query tiles (0 when the call needs neither)."""
     lib = load()
     n = ctypes.c_int64(0)
     _check(lib.bsa_fwd_workspace_size(batch, heads, num_tiles, tile, head_dim, max_sel,

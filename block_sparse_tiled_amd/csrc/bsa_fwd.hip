@@ -150,13 +150,52 @@ __device__ __forceinline__ void store_tile_rows(const f32x16_t* acc, float m_run
     }
 }
 
+// Persistent launch (kPersistent): one round of workgroups, each taking work
+// units from queues instead of one unit per dispatched workgroup.  With many
+// short units of uneven cost (one round of workgroups per 4 or more rounds of
+// units), dispatch in linear order leaves slots idle: a slot freed on one XCD
+// waits until the workgroups ahead of its next one have found free slots on
+// the other XCDs.  next_unit() returns the linear id that a one-unit launch
+// would have given the unit (so the XCD renumbering applies unchanged), or -1
+// once every queue is empty.  Queue x holds the ids x, x + 8, x + 16, ... below
+// `units` in order, behind an atomic counter; a workgroup draws from the queue
+// of its own XCD (its linear id mod 8, the dispatch order) and, once that is
+// empty, from the others in turn.  Units are independent, so which workgroup
+// runs one does not change a bit of the result.
+__device__ __forceinline__ int next_unit(uint32_t* __restrict__ queue, int units, int& xq,
+                                         int* s_unit) {
+  __syncthreads();  // every thread has read the previous unit
+  if (threadIdx.x == 0) {
+    int L = -1;
+    for (int tries = 0; tries < 8; ++tries) {
+      const int x = (xq + tries) & 7;
+      const uint32_t kq = atomicAdd(queue + 16 * x, 1u);  // counters 64 bytes apart
+      const int64_t Lc = 8 * static_cast<int64_t>(kq) + x;
+      if (Lc < units) {
+        L = static_cast<int>(Lc);
+        xq = x;
+        break;
+      }
+    }
+    *s_unit = L;
+  }
+  __syncthreads();
+  return *s_unit;
+}
+
+// Zeroes the queue counters (kFwdQueueBytes) before a persistent launch: a
+// kernel, so that the pair can be captured into a graph.
+__global__ void clear_queue_kernel(uint32_t* __restrict__ queue) {
+  if (threadIdx.x < bsa::kFwdQueueBytes / 4) queue[threadIdx.x] = 0u;
+}
+
 // kTrain: the forward of the training path (bsa_fwd_lse).  It writes the
 // log-sum-exp and the output's rounding residual, and its exponent offset
 // follows the running max eagerly, so that a row's largest logit gets
 // p = exp2(0) = 1, which bf16 holds exactly: on a sharply peaked row the bf16
 // rounding of that one p would otherwise enter o at 2^-9 of |o| and, through
 // D = dO . o, dominate the backward's dS = P (dP - D).
-template <int T, int D, bool kTrain>
+template <int T, int D, bool kTrain, bool kPersistent>
 __global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(2, T == 128 ? 2 : 4)))
 void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                     const uint16_t* __restrict__ v, const int32_t* __restrict__ q2k_idx,
@@ -164,7 +203,7 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     uint16_t* __restrict__ out, int num_tiles, int max_sel, int n_whole,
                     int n_whole_padded, int n_split_units, int splits, float* __restrict__ ws,
                     float c, float* __restrict__ lse, uint16_t* __restrict__ out_lo,
-                    int sub_shift) {
+                    int sub_shift, uint32_t* __restrict__ queue, int total_units) {
   using C = Cfg<T, D>;
   using S = Slot<T, D>;
   __shared__ __attribute__((aligned(1024))) uint16_t ks[T * D];
@@ -174,6 +213,8 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   __shared__ int2 tl[(T == 128 ? 2 : 1) * C::kThreads];
   __shared__ int wave_count[C::kWaves];
 
+  // One work unit (linear id L); `return` ends the unit.
+  auto unit = [&](const int L) {
   // Work units: items [0, n_whole) whole, one workgroup each, dispatched
   // first; then each of the remaining items cut into `splits` list segments
   // (segment s covers list positions [s*n/splits, (s+1)*n/splits) of the
@@ -184,7 +225,6 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   // one XCD, started together on consecutive query tiles, sweep the same key
   // tiles at the same time.  The first set is padded to a multiple of 8
   // units so that the second starts on XCD 0.
-  const int L = blockIdx.x;
   const int xcd = L & 7;
   int item, seg = 0, nseg = 1, unit2 = 0;
   if (L < n_whole_padded) {
@@ -488,6 +528,19 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   slot[S::kM + wave * 64 + ln] = m_run;
   slot[S::kL + wave * 64 + ln] = l_run;
   if (tid == 0) slot[S::kAny] = any_keys ? 1.0f : 0.0f;
+  };
+
+  if constexpr (kPersistent) {
+    __shared__ int s_unit;
+    int xq = static_cast<int>(blockIdx.x & 7);
+    for (;;) {
+      const int L = next_unit(queue, total_units, xq, &s_unit);
+      if (L < 0) break;
+      unit(L);
+    }
+  } else {
+    unit(static_cast<int>(blockIdx.x));
+  }
 }
 
 // Merge of the split items: one workgroup per (item, 32-column block of the
@@ -589,10 +642,17 @@ __global__ __launch_bounds__(2 * T) void bsa_fwd_merge_kernel(
   }
 }
 
+template <int T, int D, bool kPersistent>
+const void* kernel_of(bool train) {
+  return train ? reinterpret_cast<const void*>(&bsa_fwd_kernel<T, D, true, kPersistent>)
+               : reinterpret_cast<const void*>(&bsa_fwd_kernel<T, D, false, kPersistent>);
+}
+
 template <int T, int D>
 hipError_t launch(const bsa::FwdProblem& p, hipStream_t stream) {
-  const void* fn = p.lse != nullptr ? reinterpret_cast<const void*>(&bsa_fwd_kernel<T, D, true>)
-                                    : reinterpret_cast<const void*>(&bsa_fwd_kernel<T, D, false>);
+  const bool persistent = p.queue != nullptr;
+  const void* fn = persistent ? kernel_of<T, D, true>(p.lse != nullptr)
+                              : kernel_of<T, D, false>(p.lse != nullptr);
   dim3 block(Cfg<T, D>::kThreads);
   const float c = static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(D))) * kLog2e;
   const uint16_t* q = p.q;
@@ -610,10 +670,18 @@ hipError_t launch(const bsa::FwdProblem& p, hipStream_t stream) {
   float* lse = p.lse;
   uint16_t* out_lo = p.out_lo;
   int sub_shift = p.sub_shift;
+  uint32_t* queue = p.queue;
+  int units = n_whole_padded + n_split_units;
   void* args[] = {&q, &k, &v, &idx, &num, &vbs, &out, &nt, &ms, &n_whole, &n_whole_padded,
-                  &n_split_units, &splits, &ws, &cc, &lse, &out_lo, &sub_shift};
-  const int units = n_whole_padded + n_split_units;
-  hipError_t err = hipLaunchKernel(fn, dim3(static_cast<unsigned>(units)), block, args, 0, stream);
+                  &n_split_units, &splits, &ws, &cc, &lse, &out_lo, &sub_shift, &queue, &units};
+  unsigned grid = static_cast<unsigned>(units);
+  if (persistent) {
+    hipLaunchKernelGGL(clear_queue_kernel, dim3(1), dim3(bsa::kFwdQueueBytes / 4), 0, stream, queue);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    if (p.grid < units) grid = static_cast<unsigned>(p.grid);
+  }
+  hipError_t err = hipLaunchKernel(fn, dim3(grid), block, args, 0, stream);
   if (err != hipSuccess || splits <= 1 || n_split_units == 0) return err;
   const void* merge = reinterpret_cast<const void*>(&bsa_fwd_merge_kernel<T, D>);
   const float* wsc = ws;
@@ -632,18 +700,19 @@ hipError_t launch(const bsa::FwdProblem& p, hipStream_t stream) {
 // code objects, the same on every gfx950, queried once and kept in an atomic
 // (so that later plans, also those made while a stream is being captured into
 // a graph, make no runtime call).  The smaller of the two variants' counts, so
-// that bsa_fwd and bsa_fwd_lse make the same plan and need the same workspace.
-template <int T, int D>
+// that bsa_fwd and bsa_fwd_lse make the same plan and need the same workspace;
+// kPersistent: of the persistent kernels, whose count sizes their grid.
+template <int T, int D, bool kPersistent>
 hipError_t blocks_per_cu(int* per_cu) {
   static std::atomic<int> cached{0};
   int n = cached.load(std::memory_order_acquire);
   if (n == 0) {
     int a = 0, b = 0;
     hipError_t err = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &a, reinterpret_cast<const void*>(&bsa_fwd_kernel<T, D, false>), Cfg<T, D>::kThreads, 0);
+        &a, kernel_of<T, D, kPersistent>(false), Cfg<T, D>::kThreads, 0);
     if (err != hipSuccess) return err;
     err = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &b, reinterpret_cast<const void*>(&bsa_fwd_kernel<T, D, true>), Cfg<T, D>::kThreads, 0);
+        &b, kernel_of<T, D, kPersistent>(true), Cfg<T, D>::kThreads, 0);
     if (err != hipSuccess) return err;
     n = a < b ? a : b;
     if (n < 1) n = 1;
@@ -656,7 +725,7 @@ hipError_t blocks_per_cu(int* per_cu) {
 template <int T, int D>
 hipError_t plan(const bsa::FwdProblem& p, bsa::FwdPlan* plan) {
   int per_cu = 0;
-  const hipError_t err = blocks_per_cu<T, D>(&per_cu);
+  hipError_t err = blocks_per_cu<T, D, false>(&per_cu);
   if (err != hipSuccess) return err;
   const int64_t resident = static_cast<int64_t>(per_cu) * p.num_cus;
   const int64_t items = p.batch_heads * p.num_tiles;
@@ -668,7 +737,21 @@ hipError_t plan(const bsa::FwdProblem& p, bsa::FwdPlan* plan) {
   plan->splits = static_cast<int32_t>(s);
   plan->n_whole = static_cast<int32_t>(s > 1 ? items - left : items);
   plan->n_split_units = static_cast<int32_t>(s > 1 ? left * s : 0);
-  plan->ws_bytes = static_cast<size_t>(plan->n_split_units) * Slot<T, D>::kFloats * sizeof(float);
+  // Persistent launch from four rounds of units on (one round of workgroups
+  // taking units from per-XCD queues): measured faster with many rounds of
+  // short units of uneven cost (24 rounds: 8-10 %, 6 rounds: 5 %), slower with
+  // two or three rounds of long ones (1-2 %).
+  const int64_t units = (plan->n_whole + 7) / 8 * 8 + plan->n_split_units;
+  plan->persistent = units > 4 * resident ? 1 : 0;
+  plan->grid = 0;
+  if (plan->persistent) {
+    int per_cu_p = 0;
+    err = blocks_per_cu<T, D, true>(&per_cu_p);
+    if (err != hipSuccess) return err;
+    plan->grid = static_cast<int32_t>(static_cast<int64_t>(per_cu_p) * p.num_cus);
+  }
+  plan->ws_bytes = (plan->persistent ? bsa::kFwdQueueBytes : 0) +
+                   static_cast<size_t>(plan->n_split_units) * Slot<T, D>::kFloats * sizeof(float);
   return hipSuccess;
 }
 

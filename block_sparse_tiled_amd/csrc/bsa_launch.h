@@ -27,6 +27,8 @@ struct FwdProblem {
   int32_t n_split_units;  // the other items, `splits` list segments each
   int32_t splits;
   float* ws;              // n_split_units partial slots (when splits > 1)
+  uint32_t* queue;        // per-XCD work-queue counters: persistent launch; null: one unit per workgroup
+  int32_t grid;           // workgroups of a persistent launch
   float* lse;             // [B, H, NT*T] log-sum-exp per row, or null
   uint16_t* out_lo;       // [B, H, NT*T, D] bf16 rounding residual of out (with lse)
   int32_t sub_shift;      // 1: the lists and lengths count tiles of 2*tile rows
@@ -34,11 +36,17 @@ struct FwdProblem {
 
 // How the items are cut into work units, and the workspace that needs (none
 // when no item is split).
+// Bytes of per-XCD work-queue counters at the front of a persistent launch's
+// workspace (8 counters, 64 bytes apart).
+constexpr size_t kFwdQueueBytes = 512;
+
 struct FwdPlan {
   int32_t n_whole;
   int32_t n_split_units;
   int32_t splits;
-  size_t ws_bytes;
+  int32_t persistent;  // one round of workgroups taking units from per-XCD queues
+  int32_t grid;        // its workgroups
+  size_t ws_bytes;     // queue counters (persistent), then the split partials
 };
 
 hipError_t plan_fwd(const FwdProblem& p, FwdPlan* plan);

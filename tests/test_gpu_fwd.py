@@ -343,6 +343,80 @@ def test_workspace_choices(oracle_mod):
     assert bool((sentinel == 7.0).all()), "a refused call writes nothing"
 
 
+# Shapes with more than four rounds of query tiles for the resident workgroups of a
+# 256-CU MI355X (T = D = 128: 512 resident, 2400 items; T = D = 64: 2048 resident,
+# 9600 items), whose last round is at least half full (no list is cut).
+PERSISTENT = {
+    (128, 128): dict(H=40, vbs=[128] * 59 + [77], counts=10),
+    (64, 64): dict(H=24, vbs=[64] * 399 + [41], counts=8),
+}
+
+
+@pytest.mark.parametrize("T,D", sorted(PERSISTENT))
+def test_persistent_launch_same_bits_as_one_tile_per_workgroup(oracle_mod, T, D):
+    """Four or more rounds of query tiles run as one round of workgroups taking tiles
+    from per-XCD queues whose counters are the whole workspace (512 bytes): the same
+    bits as the launch without a workspace (one query tile per workgroup), the same
+    bits through bsa_fwd_noalloc, and the oracle's values on sampled rows."""
+    import torch
+
+    cfg = PERSISTENT[(T, D)]
+    w = gen.random_problem(71 + T, B=1, H=cfg["H"], D=D, T=T, vbs=cfg["vbs"], counts=cfg["counts"],
+                           pad="naninf")
+    print(f"persistent T={T} D={D}: {w.B * w.H * w.NT} query tiles", flush=True)
+    assert bsa.workspace_size(w.B, w.H, w.NT, w.T, w.D, w.MS) == 512
+    args = _launch_args(w)
+    pers = bits_from_dev(bsa.fwd(*args, w.T))
+    one = bits_from_dev(bsa.fwd(*args, w.T, workspace=None))
+    np.testing.assert_array_equal(pers, one)
+    out = torch.empty_like(args[0])
+    bsa.fwd_noalloc(*args, w.T, out)
+    np.testing.assert_array_equal(bits_from_dev(out), pers)
+    rows = sample_rows(w, 256, np.random.default_rng(5))
+    ref = oracle_mod.fwd_rows(w.q, w.k, w.v, w.q2k_idx, w.q2k_num, w.vbs, w.T, rows)
+    compare(pers.reshape(-1, D)[rows], ref, label=f"persistent T={T} D={D}")
+    assert np.all(pers[padding_rows(w)] == 0)
+
+
+def test_persistent_launch_with_cut_lists_and_graph_replays(oracle_mod):
+    """More than four rounds of query tiles AND a last round less than half full: the
+    workspace holds the queue counters and the partials of the cut lists.  Matches
+    the oracle on sampled rows; captured into a graph (the counter-clearing kernel,
+    the forward and the merge), every replay gives the eager bits."""
+    import torch
+
+    w = gen.random_problem(73, B=1, H=8, D=128, T=128, vbs=[128] * 280 + [50], counts=12)
+    print(f"persistent with cut lists: {w.B * w.H * w.NT} query tiles", flush=True)
+    need = bsa.workspace_size(w.B, w.H, w.NT, w.T, w.D, w.MS)
+    assert need > 512
+    args = _launch_args(w)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(args[0])
+    bsa.fwd(*args, w.T, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    eager = bits_from_dev(out)
+    rows = sample_rows(w, 256, np.random.default_rng(6))
+    ref = oracle_mod.fwd_rows(w.q, w.k, w.v, w.q2k_idx, w.q2k_num, w.vbs, w.T, rows)
+    compare(eager.reshape(-1, w.D)[rows], ref, label="persistent, cut lists")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        bsa.fwd(*args, w.T, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    for r in range(3):
+        out.fill_(float("nan"))
+        ws.fill_(255)  # stale counters and partials: the call clears and rewrites what it uses
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits_from_dev(out), eager, err_msg=f"replay {r}")
+        bsa.fwd(*args, w.T, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits_from_dev(out), eager, err_msg=f"eager after replay {r}")
+
+
 def test_split_lists_on_two_concurrent_streams(oracle_mod):
     """Launches on different streams may overlap; each call has its own workspace."""
     import torch
