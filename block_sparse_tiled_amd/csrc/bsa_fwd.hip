@@ -208,10 +208,11 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   using S = Slot<T, D>;
   __shared__ __attribute__((aligned(1024))) uint16_t ks[T * D];
   __shared__ __attribute__((aligned(1024))) uint16_t vs[T * D];
-  // usable list entries of the current chunk, (tile, length); two per list
-  // entry when the lists name tiles of 2T rows
-  __shared__ int2 tl[(T == 128 ? 2 : 1) * C::kThreads];
-  __shared__ int wave_count[C::kWaves];
+  // the steps of the current chunk (compact_steps): two int2 per step, at
+  // most one step per T-row part of a list entry (two parts per entry when
+  // the lists name tiles of 2T rows)
+  __shared__ int2 st[2 * (T == 128 ? 2 : 1) * C::kThreads];
+  __shared__ int wave_count[2 * C::kWaves];
 
   // One work unit (linear id L); `return` ends the unit.
   auto unit = [&](const int L) {
@@ -322,13 +323,37 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
   };
 
-  // One tile of vk valid keys (1 <= vk <= T).  On entry K(j) is in LDS and
-  // visible, V(j) may be in flight; on exit K(j2) is in LDS and visible and
-  // V(j2) is requested.  Every tile takes the full-size step (all T/32 key
-  // blocks): keys at or past vk are masked, and a single step keeps the
-  // accumulators in one register assignment across the loop (a second,
-  // half-size step made the compiler move all of them every tile).
-  auto tile_step = [&](int vk, int j2, int vk2) {
+  // The copy of step n = (j, vk) into the K or V buffer: one tile (j >= 0)
+  // or a pair of short tiles (j <= -2, the rest of the step in st[2n + 1]);
+  // j = -1: no step.  The pair's test sits behind the single tile's, so a
+  // list of whole tiles runs the same instructions as without pairs.
+  auto copy_step = [&](auto is_v, auto skip, int n, int j, int vk) {
+    constexpr bool kV = decltype(is_v)::value, kSkip = decltype(skip)::value;
+    const uint16_t* head = kV ? vh : kh;
+    uint16_t* buf = kV ? vs : ks;
+    const auto& dl = [&]() -> const auto& {
+      if constexpr (kV)
+        return v_dma;
+      else
+        return k_dma;
+    }();
+    if (j >= 0) {
+      dma_tile<T, D, kV, kSkip>(head + static_cast<int64_t>(j) * T * D, buf, wave, dl, vk);
+    } else if (j <= -2) {
+      const int2 bv = st[2 * n + 1];
+      const int jb = __builtin_amdgcn_readfirstlane(bv.x), va = __builtin_amdgcn_readfirstlane(bv.y);
+      dma_pair<T, D, kV, kSkip>(head, -2 - j, va, jb, vk - va, buf, wave, lane, dl);
+    }
+  };
+
+  // One step of vk valid keys (1 <= vk <= T): a tile, or two short tiles
+  // packed into the first vk rows of the buffers.  On entry its K is in LDS
+  // and visible, its V may be in flight; on exit the K of step n2 = (j2, vk2)
+  // is in LDS and visible and its V is requested.  Every step is full-size
+  // (all T/32 key blocks): keys at or past vk are masked, and a single step
+  // keeps the accumulators in one register assignment across the loop (a
+  // second, half-size step made the compiler move all of them every tile).
+  auto tile_step = [&](int vk, int n2, int j2, int vk2) {
     constexpr int NKB = C::kKeyBlocks;
 
     // ---- S^T = K_j Q^T, k-step outer: NKB independent accumulators, the
@@ -350,7 +375,7 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     wait_vmcnt<0>();  // V(j) (the only copy in flight)
     if (vk < T) zero_padding_rows<T, D>(vs, vk, wave, lane);
     lds_barrier();  // every wave is done with K(j); V(j) is visible
-    if (j2 >= 0) dma_tile<T, D, false, true>(kh + static_cast<int64_t>(j2) * T * D, ks, wave, k_dma, vk2);
+    copy_step(Flag<false>{}, Flag<true>{}, n2, j2, vk2);
 
     // ---- mask keys at or past vk (whole blocks included), running max ------------
     if (active) {
@@ -471,38 +496,40 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     __builtin_amdgcn_s_setprio(0);
     }  // active
 
-    // ---- K(j2) landed (the only copy in flight); every wave is done with V(j) ------
-    if (j2 >= 0) wait_vmcnt<0>();
+    // ---- K of step n2 landed (the only copy in flight); every wave is done with V ----
+    if (j2 != -1) wait_vmcnt<0>();
     lds_barrier();
-    if (j2 >= 0) dma_tile<T, D, true, true>(vh + static_cast<int64_t>(j2) * T * D, vs, wave, v_dma, vk2);
+    copy_step(Flag<true>{}, Flag<true>{}, n2, j2, vk2);
   };
 
-  // The segment in chunks of kThreads list entries; within a chunk the tiles
-  // are pipelined (the copies of the next tile overlap the current one).
+  // The segment in chunks of kThreads list entries; within a chunk the steps
+  // are pipelined (the copies of the next step overlap the current one).
   for (int base = a; base < end; base += C::kThreads) {
-    const int total = compact_list<T, C::kWaves>(list, base, end, vbs, nt_list, tl, wave_count, tid,
-                                                 wave, lane, sub_shift);
+    const int total = compact_steps<T, C::kWaves>(list, base, end, vbs, nt_list, st, wave_count, tid,
+                                                  wave, lane, sub_shift);
     if (total == 0) continue;
     any_keys = true;
-    int2 e = tl[0];
+    int2 e = st[0];
     const int j0 = __builtin_amdgcn_readfirstlane(e.x);
     int vk = __builtin_amdgcn_readfirstlane(e.y);
     // Q must be in registers before the first tile DMA is issued: the DMAs
     // are invisible to the compiler's wait-count bookkeeping, and an explicit
     // drain here keeps it from placing waits for Q inside the tile loop.
     wait_vmcnt<0>();
-    dma_tile<T, D, false>(kh + static_cast<int64_t>(j0) * T * D, ks, wave, k_dma, vk);
-    dma_tile<T, D, true>(vh + static_cast<int64_t>(j0) * T * D, vs, wave, v_dma, vk);
-    wait_vmcnt<C::kDmaPerTile>();  // K(j0) has landed (V(j0) may be in flight)
+    copy_step(Flag<false>{}, Flag<false>{}, 0, j0, vk);
+    copy_step(Flag<true>{}, Flag<false>{}, 0, j0, vk);
+    // the first step's K has landed (its V may be in flight: at least
+    // kDmaPerTile copies, one more when a pair's split block is copied twice)
+    wait_vmcnt<C::kDmaPerTile>();
     lds_barrier();
     for (int t = 0; t < total; ++t) {
       int j2 = -1, vk2 = 0;
       if (t + 1 < total) {
-        e = tl[t + 1];
+        e = st[2 * (t + 1)];
         j2 = __builtin_amdgcn_readfirstlane(e.x);
         vk2 = __builtin_amdgcn_readfirstlane(e.y);
       }
-      tile_step(vk, j2, vk2);
+      tile_step(vk, t + 1, j2, vk2);
       vk = vk2;
     }
   }

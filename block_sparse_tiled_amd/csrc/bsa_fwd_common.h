@@ -138,6 +138,12 @@ __device__ __forceinline__ float launder_f(float x) {
   return x;
 }
 
+// A compile-time flag for generic lambdas.
+template <bool B>
+struct Flag {
+  static constexpr bool value = B;
+};
+
 // Per-lane byte offsets of a wave's tile copies.  Instruction it of wave w
 // fills 1 KiB block blk = it*kWaves + w, whose global offset is the lane
 // offset of swizzle phase blk % kPeriod plus (blk - blk % kPeriod) KiB.  Of
@@ -204,6 +210,50 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, uint1
   }
 }
 
+// The copy of a step that packs two short key tiles (otherwise as
+// dma_tile): rows [0, va) of the buffer from tile ja and rows [va, va + vb)
+// from rows [0, vb) of tile jb, so that the step's valid keys are its first
+// va + vb rows and every row after them is padding, as for one short tile.
+// Two descriptors: tile ja's covering va rows, and one based va rows before
+// tile jb covering va + vb rows, so that the usual offsets of buffer rows
+// [va, va + vb) land on tile jb's rows [0, vb).  A block wholly before row va
+// copies through the first, a block wholly after it through the second; the
+// block that holds row va is copied twice, every lane active (EXEC) in exactly
+// one of the two instructions, so each writes only its own lanes' LDS slots.
+// Every address stays inside tile ja or tile jb.
+template <int T, int D, bool kIsV, bool kSkipPadding = false>
+__device__ __forceinline__ void dma_pair(const uint16_t* __restrict__ head, int ja, int va, int jb,
+                                         int vb, uint16_t* lds, int wave, int lane,
+                                         const DmaLane<T, D, kIsV>& dl) {
+  using C = Cfg<T, D>;
+  using DL = DmaLane<T, D, kIsV>;
+  constexpr int kRowsPerBlock = 512 / D;  // rows in one 1 KiB block
+  const uint32_t base = launder_s(__builtin_amdgcn_readfirstlane(lds_address(lds)) + wave * 1024);
+  const uint64_t ga = reinterpret_cast<uintptr_t>(head + static_cast<int64_t>(ja) * T * D);
+  const uint64_t gb = reinterpret_cast<uintptr_t>(head + static_cast<int64_t>(jb) * T * D) -
+                      static_cast<uint64_t>(va) * D * 2;
+  const i32x4_t srd_a = {static_cast<int>(static_cast<uint32_t>(ga)),
+                         static_cast<int>(static_cast<uint32_t>(ga >> 32)), va * D * 2, 0x00020000};
+  const i32x4_t srd_b = {static_cast<int>(static_cast<uint32_t>(gb)),
+                         static_cast<int>(static_cast<uint32_t>(gb >> 32)), (va + vb) * D * 2, 0x00020000};
+  const int lane_row = launder(lane) / C::kChunks;
+#pragma unroll
+  for (int it = 0; it < C::kDmaPerTile; ++it) {
+    const int row0 = (it * C::kWaves + wave) * kRowsPerBlock;
+    if (kSkipPadding && row0 >= va + vb) break;
+    const uint32_t soff = it * C::kWaves * 1024;
+    const uint32_t off = dl.off[it % DL::kN];
+    if (row0 + kRowsPerBlock <= va) {
+      dma16(srd_a, off, soff, base + soff);
+    } else if (row0 >= va) {
+      dma16(srd_b, off, soff, base + soff);
+    } else {  // the block holding row va (a uniform test), then split by lane
+      if (lane_row < va - row0) dma16(srd_a, off, soff, base + soff);
+      if (lane_row >= va - row0) dma16(srd_b, off, soff, base + soff);
+    }
+  }
+}
+
 // Zero the slots of padding rows (row >= vk) that this lane's own DMA wrote.
 // Slot p = 64*blk + lane holds row (64*blk + lane) / kChunks: a per-lane row
 // plus a uniform one, and a per-lane address plus an immediate offset.
@@ -262,6 +312,77 @@ __device__ __forceinline__ int compact_list(const int32_t* __restrict__ list, in
     tl[off + pos + t] = make_int2((jj << sub_shift) + t, len - T * t < T ? len - T * t : T);
   lds_barrier();
   return __builtin_amdgcn_readfirstlane(total);
+}
+
+// The steps of the forward's tile loop for list[base, min(base + 64*NW, count)):
+// the usable entries (index in range, at least one valid key) cut into T-row
+// parts as compact_list does; the parts of more than T/2 rows first, one step
+// each, then the parts of at most T/2 rows, two to a step (the last one alone
+// when their number is odd); each group keeps list order.  Step n is the int2
+// st[2n] = (j, vk): one tile j >= 0 with vk valid rows, or, for a pair,
+// j = -2 - ja and vk = va + vb, with st[2n + 1] = (jb, va).  Short part q goes
+// to step n_long + q / 2, so every part's place follows from two prefix
+// counts (mbcnt plus per-wave offsets), as in compact_list; a pair's second
+// part then adds its length to the pair's vk, after a barrier of its own
+// (taken only when there is a pair).  wave_count holds 2 * NW ints.  Returns
+// the number of steps (uniform).
+template <int T, int NW>
+__device__ __forceinline__ int compact_steps(const int32_t* __restrict__ list, int base, int count,
+                                             const int32_t* __restrict__ vbs, int num_tiles,
+                                             int2* st, int* wave_count, int tid, int wave, int lane,
+                                             int sub_shift) {
+  constexpr int kH = T / 2;
+  const int e = base + tid;
+  int jj = -1, len = 0;
+  if (e < count) {
+    jj = list[e];
+    if (jj >= 0 && jj < num_tiles) len = clampi(vbs[jj], 0, T << sub_shift);
+  }
+  // part 0 has min(len, T) rows; part 1 (lists of 2T-row tiles) len - T
+  const int len1 = len - T;
+  const bool long0 = len > kH, short0 = len > 0 && len <= kH;
+  const bool long1 = len1 > kH, short1 = len1 > 0 && len1 <= kH;
+  const uint64_t ml0 = __ballot(long0), ml1 = __ballot(long1);
+  const uint64_t ms0 = __ballot(short0), ms1 = __ballot(short1);
+  lds_barrier();  // the previous chunk's readers of st[] and wave_count[] are done
+  if (lane == 0) {
+    wave_count[2 * wave] = __popcll(ml0) + __popcll(ml1);
+    wave_count[2 * wave + 1] = __popcll(ms0) + __popcll(ms1);
+  }
+  lds_barrier();
+  int off_l = 0, off_s = 0, n_long = 0, n_short = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int cl = wave_count[2 * w], cs = wave_count[2 * w + 1];
+    off_l += w < wave ? cl : 0;
+    off_s += w < wave ? cs : 0;
+    n_long += cl;
+    n_short += cs;
+  }
+  auto below = [&](uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
+  };
+  const int pl = off_l + below(ml0) + below(ml1);  // this entry's first long part
+  const int ps = off_s + below(ms0) + below(ms1);  // its short part (an entry has at most one)
+  const int tile0 = jj << sub_shift;
+  if (long0) st[2 * pl] = make_int2(tile0, len < T ? len : T);
+  if (long1) st[2 * (pl + 1)] = make_int2(tile0 + 1, len1 < T ? len1 : T);
+  const bool is_short = short0 || short1;
+  const int step = n_long + (ps >> 1);
+  const int stile = short0 ? tile0 : tile0 + 1, slen = short0 ? len : len1;
+  if (is_short && (ps & 1) == 0)  // a pair's first part, or the last part alone
+    st[2 * step] = ps == n_short - 1 ? make_int2(stile, slen) : make_int2(-2 - stile, slen);
+  if (n_short >= 2) {  // uniform
+    lds_barrier();
+    if (is_short && (ps & 1)) {  // a pair's second part: its first part's length is in place
+      const int va = st[2 * step].y;
+      st[2 * step].y = va + slen;
+      st[2 * step + 1] = make_int2(stile, va);
+    }
+  }
+  lds_barrier();
+  return __builtin_amdgcn_readfirstlane(n_long + ((n_short + 1) >> 1));
 }
 
 // max(m, a, b), ignoring quiet NaNs.  Written as asm because the compiler

@@ -106,6 +106,16 @@ CASES = {
     # index rows far wider than the lists they hold: list segments past the
     # count are empty when the last round is split
     "wide_rows": (1, 2, lambda T: [T] * 6 + [T - 9], dict(density=0.3, MS=1000)),
+    # tiles of at most T/2 rows, which share steps two by two: lengths 1, T/2 - 1
+    # and T/2, and lengths whose end falls inside a 1 KiB copy block
+    "short_tiles": (2, 2, lambda T: [1, T // 2, T // 2 - 1, 3, 5, T // 4 + 1, T, T // 2 + 1, 9, 2, T // 2,
+                                     17, T - 2, 6], dict(density=0.7, pad="naninf")),
+    # only short tiles, an odd number of them in every list (one step holds one)
+    "short_only_odd": (1, 3, lambda T: [T // 2, 1, T // 2 - 3, 4, 7, T // 2, 13, 2, 11],
+                       dict(counts=9, pad="nan")),
+    # short tiles over several list chunks, repeated (a tile paired with itself)
+    "short_long_lists": (1, 1, lambda T: [3, T // 2, T, 6, T // 2 - 1, 0, 1],
+                         dict(counts=300, MS=300, duplicates=True, pad="inf")),
 }
 
 
@@ -130,6 +140,31 @@ def test_padding_contents_do_not_change_a_bit(T, D):
             gen.fill_padding(x, w.vbs, T, pattern)
         print(f"padding pattern {pattern}", flush=True)
         np.testing.assert_array_equal(run_fwd(w, q=q, k=k, v=v), base)
+
+
+def test_short_halves_of_256_row_tiles(oracle_mod):
+    """256-row tiles run as 128-row halves: a half of at most 64 rows (the second half
+    of a tile of 129..192 rows, or a tile of at most 64) shares a step with another."""
+    T, D = 256, 128
+    w = gen.random_problem(48, B=1, H=3, D=D, T=T, vbs=[256, 129, 192, 190, 64, 40, 1, 128, 0, 255],
+                           density=0.8, pad="naninf")
+    print(f"tile 256 short halves: NT={w.NT}", flush=True)
+    compare(run_fwd(w), oracle_out(oracle_mod, w), label="tile 256 short halves")
+
+
+def test_split_lists_of_short_tiles(oracle_mod):
+    """Lists cut into segments (partials merged by a second launch) whose tiles are
+    mostly short: each segment pairs its own short tiles."""
+    import torch
+
+    w = gen.random_problem(49, B=1, H=2, D=128, T=128, vbs=[40] * 20 + [90, 64, 64, 1], density=0.8,
+                           pad="naninf")
+    args = _launch_args(w)
+    assert bsa.workspace_size(w.B, w.H, w.NT, w.T, w.D, w.MS) > 0, "this shape is meant to split its lists"
+    ref = oracle_out(oracle_mod, w)
+    compare(bits_from_dev(bsa.fwd(*args, w.T)), ref, label="split lists, short tiles")
+    compare(bits_from_dev(bsa.fwd(*args, w.T, workspace=None)), ref, label="whole query tiles, short tiles")
+    torch.cuda.synchronize()
 
 
 def test_nan_filled_output_buffer_is_overwritten():
