@@ -212,7 +212,8 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   // most one step per T-row part of a list entry (two parts per entry when
   // the lists name tiles of 2T rows)
   __shared__ int2 st[2 * (T == 128 ? 2 : 1) * C::kThreads];
-  __shared__ int wave_count[2 * C::kWaves];
+  __shared__ int2 srt[(T == 128 ? 2 : 1) * C::kThreads];  // the parts by length (compact_steps)
+  __shared__ int wave_scratch[5 * C::kWaves];
 
   // One work unit (linear id L); `return` ends the unit.
   auto unit = [&](const int L) {
@@ -323,10 +324,11 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
   };
 
-  // The copy of step n = (j, vk) into the K or V buffer: one tile (j >= 0)
-  // or a pair of short tiles (j <= -2, the rest of the step in st[2n + 1]);
-  // j = -1: no step.  The pair's test sits behind the single tile's, so a
-  // list of whole tiles runs the same instructions as without pairs.
+  // The copy of step n = (j, vk) into the K or V buffer: one tile (j >= 0) or
+  // a pair of tiles that fit in T rows together (j <= -2, the rest of the step
+  // in st[2n + 1]); j = -1: no step.  The pair's test sits behind the single
+  // tile's, so a list of whole tiles runs the same instructions as without
+  // pairs.
   auto copy_step = [&](auto is_v, auto skip, int n, int j, int vk) {
     constexpr bool kV = decltype(is_v)::value, kSkip = decltype(skip)::value;
     const uint16_t* head = kV ? vh : kh;
@@ -346,8 +348,8 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
   };
 
-  // One step of vk valid keys (1 <= vk <= T): a tile, or two short tiles
-  // packed into the first vk rows of the buffers.  On entry its K is in LDS
+  // One step of vk valid keys (1 <= vk <= T): a tile, or two tiles packed
+  // into the first vk rows of the buffers.  On entry its K is in LDS
   // and visible, its V may be in flight; on exit the K of step n2 = (j2, vk2)
   // is in LDS and visible and its V is requested.  Every step is full-size
   // (all T/32 key blocks): keys at or past vk are masked, and a single step
@@ -505,8 +507,8 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   // The segment in chunks of kThreads list entries; within a chunk the steps
   // are pipelined (the copies of the next step overlap the current one).
   for (int base = a; base < end; base += C::kThreads) {
-    const int total = compact_steps<T, C::kWaves>(list, base, end, vbs, nt_list, st, wave_count, tid,
-                                                  wave, lane, sub_shift);
+    const int total = compact_steps<T, C::kWaves>(list, base, end, vbs, nt_list, st, srt, wave_scratch,
+                                                  tid, wave, lane, sub_shift);
     if (total == 0) continue;
     any_keys = true;
     int2 e = st[0];

@@ -210,10 +210,11 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, uint1
   }
 }
 
-// The copy of a step that packs two short key tiles (otherwise as
-// dma_tile): rows [0, va) of the buffer from tile ja and rows [va, va + vb)
-// from rows [0, vb) of tile jb, so that the step's valid keys are its first
-// va + vb rows and every row after them is padding, as for one short tile.
+// The copy of a step that packs two key tiles of va + vb <= T valid rows
+// (otherwise as dma_tile): rows [0, va) of the buffer from tile ja and rows
+// [va, va + vb) from rows [0, vb) of tile jb, so that the step's valid keys
+// are its first va + vb rows and every row after them is padding, as for one
+// short tile.
 // Two descriptors: tile ja's covering va rows, and one based va rows before
 // tile jb covering va + vb rows, so that the usual offsets of buffer rows
 // [va, va + vb) land on tile jb's rows [0, vb).  A block wholly before row va
@@ -316,73 +317,122 @@ __device__ __forceinline__ int compact_list(const int32_t* __restrict__ list, in
 
 // The steps of the forward's tile loop for list[base, min(base + 64*NW, count)):
 // the usable entries (index in range, at least one valid key) cut into T-row
-// parts as compact_list does; the parts of more than T/2 rows first, one step
-// each, then the parts of at most T/2 rows, two to a step (the last one alone
-// when their number is odd); each group keeps list order.  Step n is the int2
-// st[2n] = (j, vk): one tile j >= 0 with vk valid rows, or, for a pair,
-// j = -2 - ja and vk = va + vb, with st[2n + 1] = (jb, va).  Short part q goes
-// to step n_long + q / 2, so every part's place follows from two prefix
-// counts (mbcnt plus per-wave offsets), as in compact_list; a pair's second
-// part then adds its length to the pair's vk, after a barrier of its own
-// (taken only when there is a pair).  wave_count holds 2 * NW ints.  Returns
-// the number of steps (uniform).
+// parts as compact_list does.  Step n is the int2 st[2n] = (j, vk): one part,
+// tile j >= 0 with vk valid rows, or a pair, j = -2 - ja and vk = va + vb, with
+// st[2n + 1] = (jb, va).  When no two parts fit in T rows together, every part
+// is a step of its own, in list order.  Otherwise the steps hold as many pairs
+// as possible: with the parts sorted by length (ties in list order), k pairs
+// exist exactly when the 2k shortest, paired first with 2k-th, second with
+// (2k-1)-th and so on, all fit, so k is the largest such count (a binary
+// search, one ballot round each); pair i is parts i and 2k-1-i of that order
+// and the other parts follow one per step.  srt holds the sorted parts;
+// scratch holds 5 * NW ints.  Returns the number of steps (uniform).
 template <int T, int NW>
 __device__ __forceinline__ int compact_steps(const int32_t* __restrict__ list, int base, int count,
                                              const int32_t* __restrict__ vbs, int num_tiles,
-                                             int2* st, int* wave_count, int tid, int wave, int lane,
-                                             int sub_shift) {
-  constexpr int kH = T / 2;
+                                             int2* st, int2* srt, int* scratch, int tid, int wave,
+                                             int lane, int sub_shift) {
+  constexpr int kBig = 1 << 20;
   const int e = base + tid;
   int jj = -1, len = 0;
   if (e < count) {
     jj = list[e];
     if (jj >= 0 && jj < num_tiles) len = clampi(vbs[jj], 0, T << sub_shift);
   }
-  // part 0 has min(len, T) rows; part 1 (lists of 2T-row tiles) len - T
-  const int len1 = len - T;
-  const bool long0 = len > kH, short0 = len > 0 && len <= kH;
-  const bool long1 = len1 > kH, short1 = len1 > 0 && len1 <= kH;
-  const uint64_t ml0 = __ballot(long0), ml1 = __ballot(long1);
-  const uint64_t ms0 = __ballot(short0), ms1 = __ballot(short1);
-  lds_barrier();  // the previous chunk's readers of st[] and wave_count[] are done
+  const int parts = (len + T - 1) / T;  // non-empty T-row parts, a prefix of the tile
+  const int len0 = len < T ? len : T, len1 = len - T;
+  const uint64_t m1 = __ballot(parts >= 1);
+  const uint64_t m2 = __ballot(parts >= 2);
+  // the two shortest parts of the wave (len1 <= len0 when both exist)
+  int lo = parts >= 2 ? len1 : (parts >= 1 ? len0 : kBig);
+  int hi = parts >= 2 ? len0 : kBig;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const int lo2 = __shfl_xor(lo, o), hi2 = __shfl_xor(hi, o);
+    const int a = lo < lo2 ? lo2 : lo, b = hi < hi2 ? hi : hi2;
+    hi = a < b ? a : b;
+    lo = lo < lo2 ? lo : lo2;
+  }
+  int* const wave_count = scratch;  // [NW] parts, [NW, 3NW) shortest two, [3NW, 5NW) flags
+  lds_barrier();  // the previous chunk's readers of st[], srt[] and scratch[] are done
   if (lane == 0) {
-    wave_count[2 * wave] = __popcll(ml0) + __popcll(ml1);
-    wave_count[2 * wave + 1] = __popcll(ms0) + __popcll(ms1);
+    wave_count[wave] = __popcll(m1) + __popcll(m2);
+    scratch[NW + 2 * wave] = lo;
+    scratch[NW + 2 * wave + 1] = hi;
   }
   lds_barrier();
-  int off_l = 0, off_s = 0, n_long = 0, n_short = 0;
+  int off = 0, total = 0, glo = kBig, ghi = kBig;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
-    const int cl = wave_count[2 * w], cs = wave_count[2 * w + 1];
-    off_l += w < wave ? cl : 0;
-    off_s += w < wave ? cs : 0;
-    n_long += cl;
-    n_short += cs;
+    const int cw = wave_count[w];
+    off += w < wave ? cw : 0;
+    total += cw;
+    const int lo2 = scratch[NW + 2 * w], hi2 = scratch[NW + 2 * w + 1];
+    const int a = glo < lo2 ? lo2 : glo, b = ghi < hi2 ? ghi : hi2;
+    ghi = a < b ? a : b;
+    glo = glo < lo2 ? glo : lo2;
   }
   auto below = [&](uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
   };
-  const int pl = off_l + below(ml0) + below(ml1);  // this entry's first long part
-  const int ps = off_s + below(ms0) + below(ms1);  // its short part (an entry has at most one)
+  const int pos = off + below(m1) + below(m2);
   const int tile0 = jj << sub_shift;
-  if (long0) st[2 * pl] = make_int2(tile0, len < T ? len : T);
-  if (long1) st[2 * (pl + 1)] = make_int2(tile0 + 1, len1 < T ? len1 : T);
-  const bool is_short = short0 || short1;
-  const int step = n_long + (ps >> 1);
-  const int stile = short0 ? tile0 : tile0 + 1, slen = short0 ? len : len1;
-  if (is_short && (ps & 1) == 0)  // a pair's first part, or the last part alone
-    st[2 * step] = ps == n_short - 1 ? make_int2(stile, slen) : make_int2(-2 - stile, slen);
-  if (n_short >= 2) {  // uniform
+  total = __builtin_amdgcn_readfirstlane(total);
+  if (__builtin_amdgcn_readfirstlane(glo + ghi) > T) {  // no pair fits: list order
+    if (parts >= 1) st[2 * pos] = make_int2(tile0, len0);
+    if (parts >= 2) st[2 * pos + 2] = make_int2(tile0 + 1, len1);
     lds_barrier();
-    if (is_short && (ps & 1)) {  // a pair's second part: its first part's length is in place
-      const int va = st[2 * step].y;
-      st[2 * step].y = va + slen;
-      st[2 * step + 1] = make_int2(stile, va);
+    return total;
+  }
+  // the parts in list order, then each part's rank by (length, list position)
+  if (parts >= 1) st[pos] = make_int2(tile0, len0);
+  if (parts >= 2) st[pos + 1] = make_int2(tile0 + 1, len1);
+  lds_barrier();
+  int r0 = 0, r1 = 0;
+  if (parts >= 1) {
+    for (int q = 0; q < total; ++q) {
+      const int lq = st[q].y;
+      r0 += lq < len0 || (lq == len0 && q < pos);
+      r1 += lq < len1 || (lq == len1 && q < pos + 1);
     }
+    srt[r0] = make_int2(tile0, len0);
+    if (parts >= 2) srt[r1] = make_int2(tile0 + 1, len1);
   }
   lds_barrier();
-  return __builtin_amdgcn_readfirstlane(n_long + ((n_short + 1) >> 1));
+  // k: the most nested pairs of the 2k shortest that fit (at least one does)
+  int klo = 1, khi = total >> 1, it = 0;
+  while (klo < khi) {  // uniform
+    const int mid = (klo + khi + 1) >> 1;
+    const bool bad = tid < mid && srt[tid].y + srt[2 * mid - 1 - tid].y > T;
+    const uint64_t mb = __ballot(bad);
+    int* const flags = scratch + 3 * NW + (it & 1) * NW;
+    if (lane == 0) flags[wave] = mb != 0;
+    lds_barrier();
+    int any = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) any |= flags[w];
+    if (__builtin_amdgcn_readfirstlane(any))
+      khi = mid - 1;
+    else
+      klo = mid;
+    ++it;
+  }
+  const int k = klo;
+  // pair r (r < k) is written by its shorter part, which reads its partner
+  auto place = [&](int r, int tile, int l) {
+    if (r < k) {
+      const int2 big = srt[2 * k - 1 - r];
+      st[2 * r] = make_int2(-2 - big.x, big.y + l);
+      st[2 * r + 1] = make_int2(tile, big.y);
+    } else if (r >= 2 * k) {
+      st[2 * (r - k)] = make_int2(tile, l);
+    }
+  };
+  if (parts >= 1) place(r0, tile0, len0);
+  if (parts >= 2) place(r1, tile0 + 1, len1);
+  lds_barrier();
+  return total - k;
 }
 
 // max(m, a, b), ignoring quiet NaNs.  Written as asm because the compiler

@@ -116,6 +116,11 @@ CASES = {
     # short tiles over several list chunks, repeated (a tile paired with itself)
     "short_long_lists": (1, 1, lambda T: [3, T // 2, T, 6, T // 2 - 1, 0, 1],
                          dict(counts=300, MS=300, duplicates=True, pad="inf")),
+    # long tiles with the short ones that complete them to exactly T rows, and
+    # equal lengths (ties in the order by length)
+    "complementary_lengths": (2, 2, lambda T: [T - 20, 20, T - 1, 1, 3 * T // 4, T // 4, T // 2 + 5,
+                                               T // 2 - 5, T, T - 20, 20, 7],
+                              dict(density=0.8, pad="naninf")),
 }
 
 
@@ -177,8 +182,11 @@ def test_nan_filled_output_buffer_is_overwritten():
     np.testing.assert_array_equal(got, ref)
 
 
-def test_repeated_runs_are_bit_identical():
-    w = gen.make("ragged")
+@pytest.mark.parametrize("name", ["ragged", "stress"])
+def test_repeated_runs_are_bit_identical(name):
+    """Also where lists pair their tiles (stress): the pairing and the order of the
+    steps are fixed by the lengths and list positions alone."""
+    w = gen.make(name)
     a = run_fwd(w)
     b = run_fwd(w)
     np.testing.assert_array_equal(a, b)
