@@ -418,8 +418,13 @@ void dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   constexpr int NDB = C::kDBlocks;
   __shared__ __attribute__((aligned(1024))) uint16_t ks[T * D];
   __shared__ __attribute__((aligned(1024))) uint16_t vs[T * D];
-  __shared__ int2 tl[(T == 128 ? 2 : 1) * C::kThreads];  // two per entry with 2T-row lists
-  __shared__ int wave_count[C::kWaves];
+  // the steps of the current list chunk (compact_steps, as in the forward): a
+  // tile, or, at T = 128, two tiles that fit in T rows together (at T = 64 the
+  // pair's copy code made the compiler schedule the S/dP products worse)
+  constexpr bool kPairs = T == 128;
+  __shared__ int2 st[2 * (T == 128 ? 2 : 1) * C::kThreads];
+  __shared__ int2 srt[kPairs ? 2 * C::kThreads : 1];
+  __shared__ int wave_scratch[5 * C::kWaves];
 
   const int item = item_of(blockIdx.x, n_padded);
   if (item >= n_items) return;
@@ -462,8 +467,13 @@ void dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const f32x16_t zero16 = {};
 
   for (int base = 0; base < count; base += C::kThreads) {
-    const int total = compact_list<T, C::kWaves>(list, base, count, vbs, nt_list, tl, wave_count,
-                                                 tid, wave, lane, sub_shift);
+    int total;
+    if constexpr (kPairs)
+      total = compact_steps<T, C::kWaves>(list, base, count, vbs, nt_list, st, srt, wave_scratch, tid, wave,
+                                          lane, sub_shift);
+    else
+      total = compact_list<T, C::kWaves, 2>(list, base, count, vbs, nt_list, st, wave_scratch, tid, wave, lane,
+                                            sub_shift);
     if (total > 0) any_keys = true;
     // K and V are copied in 64-key halves, each as soon as its LDS half is
     // free: the next tile's half h once every wave is done with this tile's
@@ -472,10 +482,22 @@ void dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     // traffic), which keeps the vmcnt waits exact.
     constexpr int NH = T / 64;                // 64-key halves
     constexpr int kHP = C::kDmaPerTile / NH;  // copy instructions per half and tensor
-    auto copy_half = [&](auto hc, int j, int vk) {
+    // Step n = (j, vk): one tile (j >= 0), or a pair (j <= -2, the rest of the
+    // step in st[2n + 1]) whose second tile's rows follow the first's; a
+    // pair's copy may issue one instruction more per tensor (the block holding
+    // the boundary row, split by lane), which only makes later waits for
+    // earlier copies wait longer.
+    auto copy_half = [&](auto hc, int n, int j, int vk) {
       constexpr int h = decltype(hc)::value;
-      dma_tile_part<T, D, h * kHP, (h + 1) * kHP>(kh + static_cast<int64_t>(j) * T * D, ks, wave, dl, vk);
-      dma_tile_part<T, D, h * kHP, (h + 1) * kHP>(vh + static_cast<int64_t>(j) * T * D, vs, wave, dl, vk);
+      if (!kPairs || j >= 0) {
+        dma_tile_part<T, D, h * kHP, (h + 1) * kHP>(kh + static_cast<int64_t>(j) * T * D, ks, wave, dl, vk);
+        dma_tile_part<T, D, h * kHP, (h + 1) * kHP>(vh + static_cast<int64_t>(j) * T * D, vs, wave, dl, vk);
+      } else {
+        const int2 bv = st[2 * n + 1];
+        const int jb = __builtin_amdgcn_readfirstlane(bv.x), va = __builtin_amdgcn_readfirstlane(bv.y);
+        dma_pair<T, D, false, false, h * kHP, (h + 1) * kHP>(kh, -2 - j, va, jb, vk - va, ks, wave, lane, dl);
+        dma_pair<T, D, false, false, h * kHP, (h + 1) * kHP>(vh, -2 - j, va, jb, vk - va, vs, wave, lane, dl);
+      }
     };
     // Q, dO and the row statistics must be in registers before the first copy:
     // the copies are invisible to the compiler's wait-count bookkeeping, and a
@@ -484,16 +506,16 @@ void dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     // the copies in flight.
     wait_vmcnt<0>();
     for (int t = 0; t < total; ++t) {
-      const int2 e = tl[t];
+      const int2 e = st[2 * t];
       const int j = __builtin_amdgcn_readfirstlane(e.x);
       const int vk = __builtin_amdgcn_readfirstlane(e.y);
       int j2 = -1, vk2 = 0;
       if (t + 1 < total) {
-        const int2 e2 = tl[t + 1];
+        const int2 e2 = st[2 * (t + 1)];
         j2 = __builtin_amdgcn_readfirstlane(e2.x);
         vk2 = __builtin_amdgcn_readfirstlane(e2.y);
       }
-      if (t == 0) static_for<NH>([&](auto hc) { copy_half(hc, j, vk); });
+      if (t == 0) static_for<NH>([&](auto hc) { copy_half(hc, 0, j, vk); });
       static_for<NH>([&](auto hc) {  // 64 keys: key blocks 2*hh, 2*hh + 1
         constexpr int hh = decltype(hc)::value;
         // half hh of this tile has landed; issued after it: its later halves
@@ -505,7 +527,7 @@ void dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         }
         lds_barrier();  // half hh visible; every wave is done with half hh - 1
         if constexpr (hh > 0)
-          if (j2 >= 0) copy_half(std::integral_constant<int, hh - 1>{}, j2, vk2);
+          if (j2 != -1) copy_half(std::integral_constant<int, hh - 1>{}, t + 1, j2, vk2);
         if (wave * 32 < vq) {  // a wave whose rows are all padding computes nothing
         // Raised issue priority for the S/dP products: two workgroups share each
         // SIMD, and the wave in this phase winning issue pushes the pair towards
@@ -557,7 +579,7 @@ void dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         }
       });
       lds_barrier();  // every wave is done with the last half
-      if (j2 >= 0) copy_half(std::integral_constant<int, NH - 1>{}, j2, vk2);
+      if (j2 != -1) copy_half(std::integral_constant<int, NH - 1>{}, t + 1, j2, vk2);
     }
   }
   wait_vmcnt<0>();

@@ -222,7 +222,9 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, uint1
 // block that holds row va is copied twice, every lane active (EXEC) in exactly
 // one of the two instructions, so each writes only its own lanes' LDS slots.
 // Every address stays inside tile ja or tile jb.
-template <int T, int D, bool kIsV, bool kSkipPadding = false>
+// Only instructions [kLo, kHi) when given, for a caller that copies a tile in
+// parts (as dma_tile_part).
+template <int T, int D, bool kIsV, bool kSkipPadding = false, int kLo = 0, int kHi = Cfg<T, D>::kDmaPerTile>
 __device__ __forceinline__ void dma_pair(const uint16_t* __restrict__ head, int ja, int va, int jb,
                                          int vb, uint16_t* lds, int wave, int lane,
                                          const DmaLane<T, D, kIsV>& dl) {
@@ -239,7 +241,7 @@ __device__ __forceinline__ void dma_pair(const uint16_t* __restrict__ head, int 
                          static_cast<int>(static_cast<uint32_t>(gb >> 32)), (va + vb) * D * 2, 0x00020000};
   const int lane_row = launder(lane) / C::kChunks;
 #pragma unroll
-  for (int it = 0; it < C::kDmaPerTile; ++it) {
+  for (int it = kLo; it < kHi; ++it) {
     const int row0 = (it * C::kWaves + wave) * kRowsPerBlock;
     if (kSkipPadding && row0 >= va + vb) break;
     const uint32_t soff = it * C::kWaves * 1024;
@@ -279,8 +281,9 @@ __device__ __forceinline__ void zero_padding_rows(uint16_t* lds, int vk, int wav
 // each entry becomes its non-empty T-row halves (tile 2j + t, t = 0, 1), in
 // order: tl[] then holds up to 2 * 64 * NW entries.  One list entry per thread
 // of an NW-wave workgroup; the order is kept by wave-level prefix counts
-// (mbcnt) plus per-wave offsets.  Three barriers.
-template <int T, int NW>
+// (mbcnt) plus per-wave offsets.  Entry n is written to tl[kStride * n].
+// Three barriers.
+template <int T, int NW, int kStride = 1>
 __device__ __forceinline__ int compact_list(const int32_t* __restrict__ list, int base, int count,
                                             const int32_t* __restrict__ vbs, int num_tiles,
                                             int2* tl, int* wave_count, int tid, int wave,
@@ -310,7 +313,7 @@ __device__ __forceinline__ int compact_list(const int32_t* __restrict__ list, in
   };
   const int pos = below(m1) + below(m2);
   for (int t = 0; t < parts; ++t)
-    tl[off + pos + t] = make_int2((jj << sub_shift) + t, len - T * t < T ? len - T * t : T);
+    tl[kStride * (off + pos + t)] = make_int2((jj << sub_shift) + t, len - T * t < T ? len - T * t : T);
   lds_barrier();
   return __builtin_amdgcn_readfirstlane(total);
 }

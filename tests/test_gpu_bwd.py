@@ -99,6 +99,17 @@ def test_random_ragged_lists(T, D):
     check_problem(w, 1, f"random T={T} D={D}")
 
 
+@pytest.mark.parametrize("T,D", [(64, 128), (128, 64), (128, 128)])
+def test_tiles_in_pairs(T, D):
+    """Lists whose tiles share steps two by two in the forward and the dQ kernel (tiles of
+    1, T/2 - 1 and T/2 rows, long tiles with the short ones that complete them), with
+    NaN/Inf padding."""
+    vbs = [1, T // 2, T // 2 - 1, 3, min(100, T), 28, T - 1, 5, T // 2, 17, T, 40]
+    w = gen.random_problem(130 + T + D, B=1, H=2, D=D, T=T, vbs=vbs, density=0.8, pad="naninf")
+    print(f"bwd tiles in pairs T={T} D={D}", flush=True)
+    check_problem(w, 13, f"tiles in pairs T={T} D={D}")
+
+
 def test_duplicates_and_empty_tiles():
     T, D = 128, 128
     w = gen.random_problem(70, B=2, H=1, D=D, T=T, vbs=[T, 0, 77, T], counts=3, MS=3,
