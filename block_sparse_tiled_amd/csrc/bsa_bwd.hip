@@ -748,8 +748,11 @@ void dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   __shared__ __attribute__((aligned(1024))) uint16_t ds_all[2][T * D];  // dO tiles
   __shared__ __attribute__((aligned(16))) float lse_all[2][T];
   __shared__ __attribute__((aligned(16))) float dlt_all[2][T];
-  __shared__ int2 tl[(T == 128 ? 2 : 1) * C::kThreads];  // usable entries: (tile, length)
-  __shared__ int wave_count[C::kWaves];
+  // the steps of the current list chunk (compact_steps, as in the forward):
+  // a query tile, or two that fit in T rows together
+  __shared__ int2 st[2 * (T == 128 ? 2 : 1) * C::kThreads];
+  __shared__ int2 srt[(T == 128 ? 2 : 1) * C::kThreads];
+  __shared__ int wave_scratch[5 * C::kWaves];
 
   const int item = item_of(blockIdx.x, n_padded);  // (b*H + h) * NT + key tile j
   if (item >= n_items) return;
@@ -789,27 +792,13 @@ void dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const DmaLane<T, D, false> dl(wave, lane);
   const f32x16_t zero16 = {};
 
-  // Copies of usable entry t of the chunk (query tile i, vq valid rows) into
-  // buffer `buf`; its statistics go to registers (threads below T), written
-  // to LDS once they have landed.
+  // Copies of step t of the chunk into buffer `buf`; its statistics go to
+  // registers (threads below T), written to LDS once they have landed.  A step
+  // is a query tile i with vq valid rows, or a pair (i = -2 - ia): rows
+  // [0, va) of tile ia and, after them, the first vq - va rows of tile ib.
   float l_next = 0.0f, d_next = 0.0f;
   TileCopy<T, D, false> copy_q, copy_o;
-  // Statistics of entry t, and the copies' sources: `copy_q` and `copy_o`
-  // are set up to issue entry t's copies into buffer `buf`.
-  auto stage = [&](int t, int buf) {
-    const int2 e = tl[t];
-    const int i = __builtin_amdgcn_readfirstlane(e.x);
-    const int vq = __builtin_amdgcn_readfirstlane(e.y);
-    const int64_t qtile = static_cast<int64_t>(i) * T;
-    copy_q.set(qh + qtile * D, qs_all[buf], wave, vq);
-    copy_o.set(oh + qtile * D, ds_all[buf], wave, vq);
-    if (tid < vq) {
-      const int64_t r = (bh * num_tiles + i) * T + tid;
-      l_next = lse[r];
-      d_next = delta[r];
-    }
-  };
-  // Copy instruction n of the staged entry: Q's for even n, dO's for odd n.
+  // Copy instruction n of a staged single tile: Q's for even n, dO's for odd n.
   // With kSkip, blocks wholly past the valid rows are not copied; without,
   // their lanes fail the range check (no memory traffic), and what they
   // leave in LDS is zeroed with the other padding rows once the copy lands.
@@ -820,20 +809,44 @@ void dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     else copy_o.template one<n / 2, kSkip>(dl, wave);
   };
   constexpr int kCopies = 2 * C::kDmaPerTile;
-  auto issue = [&](int t, int buf) {
-    stage(t, buf);
-    static_for<kCopies>([&](auto nc) { copy_one(nc, std::true_type{}); });
+  // Stages step t: a single tile's copies are issued now, or, with `spread`,
+  // left to copy_one (returns true); a pair's are always issued now.
+  auto issue = [&](int t, int buf, bool spread) {
+    const int2 e = st[2 * t];
+    const int i = __builtin_amdgcn_readfirstlane(e.x);
+    const int vq = __builtin_amdgcn_readfirstlane(e.y);
+    int ia = i, va = vq, ib = 0;
+    if (i >= 0) {
+      const int64_t qtile = static_cast<int64_t>(i) * T;
+      copy_q.set(qh + qtile * D, qs_all[buf], wave, vq);
+      copy_o.set(oh + qtile * D, ds_all[buf], wave, vq);
+      if (!spread) static_for<kCopies>([&](auto nc) { copy_one(nc, std::true_type{}); });
+    } else {
+      const int2 bv = st[2 * t + 1];
+      ia = -2 - i;
+      ib = __builtin_amdgcn_readfirstlane(bv.x);
+      va = __builtin_amdgcn_readfirstlane(bv.y);
+      dma_pair<T, D, false, true>(qh, ia, va, ib, vq - va, qs_all[buf], wave, lane, dl);
+      dma_pair<T, D, false, true>(oh, ia, va, ib, vq - va, ds_all[buf], wave, lane, dl);
+      spread = false;
+    }
+    if (tid < vq) {
+      const int64_t r = (bh * num_tiles + (tid < va ? ia : ib)) * T + (tid < va ? tid : tid - va);
+      l_next = lse[r];
+      d_next = delta[r];
+    }
+    return spread;
   };
 
   for (int base = 0; base < count; base += C::kThreads) {
-    const int total = compact_list<T, C::kWaves>(list, base, count, vbs, nt_list, tl, wave_count,
-                                                 tid, wave, lane, sub_shift);
+    const int total = compact_steps<T, C::kWaves>(list, base, count, vbs, nt_list, st, srt, wave_scratch,
+                                                  tid, wave, lane, sub_shift);
     if (total == 0) continue;
     wait_vmcnt<0>();  // the register operands loaded above
-    issue(0, 0);
+    issue(0, 0, false);
     for (int t = 0; t < total; ++t) {
       const int buf = t & 1;
-      const int vq = __builtin_amdgcn_readfirstlane(tl[t].y);
+      const int vq = __builtin_amdgcn_readfirstlane(st[2 * t].y);
       uint16_t* qs = qs_all[buf];
       uint16_t* ds_ = ds_all[buf];
       float* lse_s = lse_all[buf];
@@ -853,12 +866,9 @@ void dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       // over tile t's products: issued as one burst they would hold it for
       // as long as the L2 -> LDS path takes to accept them.  A wave without
       // products to hide them under issues them at once.
-      const bool has_next = t + 1 < total;
       constexpr bool kSpread = D == 128;
-      if (has_next) {
-        if (!kSpread || wave * 32 >= vk) issue(t + 1, buf ^ 1);
-        else stage(t + 1, buf ^ 1);
-      }
+      bool spread_next = false;  // tile t + 1's copies are left to the steps below
+      if (t + 1 < total) spread_next = issue(t + 1, buf ^ 1, kSpread && wave * 32 < vk);
     // Per 32-query block: S = Q K^T and dP = dO V^T (steps k < NA), P and dS,
     // then dV^T += dO^T P and dK^T += Q^T dS over its two 16-query chunks
     // (steps k >= NA), in the pipelined order kDkvPipe gives.  With one wave
@@ -923,7 +933,7 @@ void dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         constexpr int kCopyEvery = kSpan < 4 ? (kSpan > 0 ? kSpan : 1) : 4;
         static_assert(!kSpread || 2 + (kCopies - 1) * kCopyEvery < kSteps, "every copy is issued");
         if constexpr (kSpread && p >= 2 && (p - 2) % kCopyEvery == 0 && (p - 2) / kCopyEvery < kCopies) {
-          if (has_next) copy_one(std::integral_constant<int, (p - 2) / kCopyEvery>{}, std::false_type{});
+          if (spread_next) copy_one(std::integral_constant<int, (p - 2) / kCopyEvery>{}, std::false_type{});
         }
         constexpr int smg = kDkvPipe<NQB, NA, NB, kSets>.sm[p];
         if constexpr (smg >= 0) {
