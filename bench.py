@@ -36,6 +36,7 @@ WORKLOAD_NAMES = {
     "stress": "stress_ragged_naninf",
     "dense25": "dense_shape_25pct",
     "dense256": "dense_limit_31200_tile256",
+    "video_cube": "video_cube_64tile",
     "tiny": "tiny",
 }
 KERNEL_SOURCES = ["bsa_fwd_common.h", "bsa_fwd.hip"]

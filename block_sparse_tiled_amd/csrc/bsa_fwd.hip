@@ -211,8 +211,12 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   // the steps of the current chunk (compact_steps): two int2 per step, at
   // most one step per T-row part of a list entry (two parts per entry when
   // the lists name tiles of 2T rows)
+  // Two key tiles share a step at T = 128 only: at T = 64 the step is bound by
+  // the tile copies, which pairing does not reduce, and the pairing's order
+  // and bookkeeping cost more than the steps it saves.
+  constexpr bool kPairs = T == 128;
   __shared__ int2 st[2 * (T == 128 ? 2 : 1) * C::kThreads];
-  __shared__ int2 srt[(T == 128 ? 2 : 1) * C::kThreads];  // the parts by length (compact_steps)
+  __shared__ int2 srt[kPairs ? 2 * C::kThreads : 1];  // the parts by length (compact_steps)
   __shared__ int wave_scratch[5 * C::kWaves];
 
   // One work unit (linear id L); `return` ends the unit.
@@ -341,7 +345,7 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }();
     if (j >= 0) {
       dma_tile<T, D, kV, kSkip>(head + static_cast<int64_t>(j) * T * D, buf, wave, dl, vk);
-    } else if (j <= -2) {
+    } else if (kPairs && j <= -2) {
       const int2 bv = st[2 * n + 1];
       const int jb = __builtin_amdgcn_readfirstlane(bv.x), va = __builtin_amdgcn_readfirstlane(bv.y);
       dma_pair<T, D, kV, kSkip>(head, -2 - j, va, jb, vk - va, buf, wave, lane, dl);
@@ -507,8 +511,13 @@ void bsa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   // The segment in chunks of kThreads list entries; within a chunk the steps
   // are pipelined (the copies of the next step overlap the current one).
   for (int base = a; base < end; base += C::kThreads) {
-    const int total = compact_steps<T, C::kWaves>(list, base, end, vbs, nt_list, st, srt, wave_scratch,
-                                                  tid, wave, lane, sub_shift);
+    int total;
+    if constexpr (kPairs)
+      total = compact_steps<T, C::kWaves>(list, base, end, vbs, nt_list, st, srt, wave_scratch, tid, wave,
+                                          lane, sub_shift);
+    else
+      total = compact_list<T, C::kWaves, 2>(list, base, end, vbs, nt_list, st, wave_scratch, tid, wave, lane,
+                                            sub_shift);
     if (total == 0) continue;
     any_keys = true;
     int2 e = st[0];

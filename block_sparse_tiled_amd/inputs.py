@@ -260,6 +260,46 @@ def video(seed=2, gate=False):
     return w
 
 
+def video_cube_tiles(dims=(21, 30, 52), cube=(4, 4, 4), n_near=8):
+    """A t x h x w latent cut into ct x ch x cw cubes, numbered row-major over the cube
+    grid: each cube's token count (edge cubes clipped) and the n_near cubes whose token
+    centroids are closest to its own (ties to the lower index; the set includes the cube).
+    Token n sits at (t, y, x), x fastest."""
+    n = np.arange(int(np.prod(dims)))
+    coords = np.stack([n // (dims[1] * dims[2]), (n // dims[2]) % dims[1], n % dims[2]], 1)
+    grid = [-(-d // c) for d, c in zip(dims, cube)]
+    cid = ((coords[:, 0] // cube[0]) * grid[1] + coords[:, 1] // cube[1]) * grid[2] + coords[:, 2] // cube[2]
+    NT = int(np.prod(grid))
+    counts = np.bincount(cid, minlength=NT)
+    cent = np.zeros((NT, 3))
+    np.add.at(cent, cid, coords.astype(np.float64))
+    cent /= counts[:, None]
+    d2 = ((cent[:, None, :] - cent[None, :, :]) ** 2).sum(-1)
+    order = np.lexsort((np.broadcast_to(np.arange(NT), d2.shape), d2), axis=1)
+    return counts.astype(np.int32), order[:, :n_near].astype(np.int32)
+
+
+def video_cube(seed=7, gate=False):
+    """The video shape in the cube tiling: B=1, H=12, D=128, the 21x30x52 latent in
+    4x4x4 cubes, one tile of 64 per cube: 455 whole cubes and 169 edge cubes of 32, 16
+    or 8 tokens; N(0, 0.5); the 8 nearest cubes plus 24 random ones per list.  Tokens are
+    drawn independently, so each cube's tokens are placed tile by tile (the cube map's
+    gather belongs to the layout step)."""
+    rng = np.random.default_rng(seed)
+    B, H, T = 1, 12, 64
+    vbs, near = video_cube_tiles((21, 30, 52), (4, 4, 4), 8)
+    NT = vbs.size
+
+    def pick(rng, b, h, i, n):
+        far = _distinct(rng, NT, n - near.shape[1], exclude=near[i])
+        return np.concatenate([near[i], far])
+
+    w = build("video_cube", B, H, 128, T, vbs, lambda rng: np.full((B, H, NT), 32, np.int32),
+              pick, rng, sigma=0.5, MS=32, gate=gate)
+    w.notes["nearest"] = near
+    return w
+
+
 def dense(seed=3, gate=False, density_tiles=None, name="dense"):
     """B=1, H=6, D=128, 31200 tokens in 244 tiles of 128 (last 96); every list holds
     every tile in order (or ``density_tiles`` random ones)."""
@@ -330,6 +370,7 @@ CONFIGS = {
     "stress": stress,
     "dense25": dense25,
     "dense256": dense256,
+    "video_cube": video_cube,
 }
 
 

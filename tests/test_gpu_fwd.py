@@ -62,7 +62,7 @@ def test_ragged_config_every_row(oracle_mod):
     print(f"ragged max {mx:.3e} mean {mean:.3e}")
 
 
-@pytest.mark.parametrize("name", ["video", "dense", "dense25", "stress", "dense256"])
+@pytest.mark.parametrize("name", ["video", "video_cube", "dense", "dense25", "stress", "dense256"])
 def test_full_size_config_sampled(oracle_mod, name):
     w = gen.make(name)
     print(f"{name}: B={w.B} H={w.H} NT={w.NT} T={w.T} MS={w.MS}", flush=True)

@@ -58,6 +58,20 @@ def test_video_recipe(page):
             assert set(near[i]) <= set(lst.tolist()) and len(set(lst.tolist())) == 32
 
 
+def test_video_cube_recipe():
+    w = gen.video_cube()
+    # 21 x 30 x 52 in 4 x 4 x 4 cubes: 6 x 8 x 13 cubes, clipped to 1 frame and 2 rows at the edges
+    assert w.NT == 6 * 8 * 13 and int(w.vbs.sum()) == 21 * 30 * 52 and w.T == 64
+    sizes, n = np.unique(w.vbs, return_counts=True)
+    assert dict(zip(sizes.tolist(), n.tolist())) == {8: 13, 16: 91, 32: 65, 64: 455}
+    assert w.vbs[0] == 64 and w.vbs[7 * 13] == 32 and w.vbs[5 * 8 * 13] == 16 and w.vbs[-1] == 8
+    near = w.notes["nearest"]
+    assert (near[:, 0] == np.arange(w.NT)).all(), "a cube is its own nearest cube"
+    for i in (0, 300, w.NT - 1):
+        lst = w.q2k_idx[0, 3, i]
+        assert set(near[i]) <= set(lst.tolist()) and len(set(lst.tolist())) == 32
+
+
 def test_dense_recipe(page):
     w = gen.dense()
     assert w.H == page["dense_shape"]["heads"]
