@@ -55,10 +55,18 @@ def full_tile_flops(w):
 
 
 def kernel_source_digest():
+    """sha256 (first 16 hex digits) of the forward kernel's sources with comments and
+    whitespace removed: a change to the code, not to its comments, makes the committed
+    traffic counters stale."""
+    import re
+
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "block_sparse_tiled_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "block_sparse_tiled_amd", "csrc", name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -318,18 +318,19 @@ __device__ __forceinline__ int compact_list(const int32_t* __restrict__ list, in
   return __builtin_amdgcn_readfirstlane(total);
 }
 
-// The steps of the forward's tile loop for list[base, min(base + 64*NW, count)):
-// the usable entries (index in range, at least one valid key) cut into T-row
-// parts as compact_list does.  Step n is the int2 st[2n] = (j, vk): one part,
-// tile j >= 0 with vk valid rows, or a pair, j = -2 - ja and vk = va + vb, with
-// st[2n + 1] = (jb, va).  When no two parts fit in T rows together, every part
-// is a step of its own, in list order.  Otherwise the steps hold as many pairs
-// as possible: with the parts sorted by length (ties in list order), k pairs
-// exist exactly when the 2k shortest, paired first with 2k-th, second with
-// (2k-1)-th and so on, all fit, so k is the largest such count (a binary
-// search, one ballot round each); pair i is parts i and 2k-1-i of that order
-// and the other parts follow one per step.  srt holds the sorted parts;
-// scratch holds 5 * NW ints.  Returns the number of steps (uniform).
+// The steps of a tile loop (the forward's; the dQ and dK/dV kernels' too) for
+// list[base, min(base + 64*NW, count)): the usable entries (index in range, at
+// least one valid key) cut into T-row parts as compact_list does.  Step n is
+// the int2 st[2n] = (j, vk): one part, tile j >= 0 with vk valid rows, or a
+// pair, j = -2 - ja and vk = va + vb, with st[2n + 1] = (jb, va).  When no two
+// parts fit in T rows together, every part is a step of its own, in list order.
+// Otherwise the steps hold as many pairs as possible: with the parts sorted by
+// length (ties in list order), k pairs exist exactly when the 2k shortest,
+// paired first with 2k-th, second with (2k-1)-th and so on, all fit, so k is
+// the largest such count (a binary search, one ballot and one barrier per
+// probe); pair i is parts i and 2k-1-i of that order and the other parts follow
+// one per step.  srt holds the sorted parts; scratch holds 5 * NW ints.
+// Returns the number of steps (uniform).
 template <int T, int NW>
 __device__ __forceinline__ int compact_steps(const int32_t* __restrict__ list, int base, int count,
                                              const int32_t* __restrict__ vbs, int num_tiles,
