@@ -28,7 +28,8 @@ def test_noalloc_matches_fwd_on_two_calls_in_a_row():
     import torch
 
     big = gen.ragged()
-    small = gen.random_problem(67, B=1, H=2, D=128, T=128, vbs=[128] * 20 + [90], density=0.8,
+    # the small one also has two short tiles, so that its lists pair tiles into steps
+    small = gen.random_problem(67, B=1, H=2, D=128, T=128, vbs=[128] * 18 + [90, 40, 20], density=0.8,
                                pad="naninf")
     cases = []
     for w in (big, small):
