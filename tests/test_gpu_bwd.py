@@ -134,6 +134,21 @@ def test_long_transposed_lists(T, D):
     check_problem(w, 12, f"long transposed lists T={T} D={D}", max_k=2 * NT)
 
 
+@pytest.mark.parametrize("T,D", [(64, 128), (128, 128)])
+def test_long_transposed_lists_of_short_query_tiles(T, D):
+    """As above, with most query tiles at most T/2 rows long: the dK/dV kernel pairs
+    them, two to a step, in every chunk of key tile 5's long transposed list, and the
+    forward and the dQ kernel pair the short key tiles of each list."""
+    NT = 4 * T + 44
+    rng = np.random.default_rng(140 + T)
+    vbs = [int(x) for x in rng.integers(1, T // 2 + 1, size=NT)]
+    vbs[5], vbs[7], vbs[NT - 2] = T, T - 3, 0
+    w = gen.random_problem(150 + T + D, B=1, H=1, D=D, T=T, vbs=vbs, counts=3, MS=3, pad="naninf")
+    w.q2k_idx[..., 0] = 5
+    print(f"bwd long transposed lists of short query tiles T={T} D={D} NT={NT}", flush=True)
+    check_problem(w, 14, f"long lists, short tiles T={T} D={D}", max_k=2 * NT)
+
+
 @pytest.mark.parametrize("B,H,NT,MS,max_k", [(2, 3, 300, 40, 50),     # counted in LDS
                                              (1, 1, 4097, 2, 4097),    # more tiles than the count holds: scan
                                              (1, 1, 1024, 1024, 64)])  # too many entries per head: scan
